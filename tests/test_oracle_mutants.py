@@ -1,0 +1,123 @@
+"""Planted mistakes in the oracle (CPU only) must each fail at least one pin.
+
+Every mutant below is a plausible slip — a dropped factor, a flipped sign,
+a swapped index or band, a strict instead of non-strict comparison, a
+transposed normalisation — patched into ``oracle`` for the duration of one
+check.  The pins in test_oracle_rope / test_oracle_attention must reject it.
+"""
+import numpy as np
+import pytest
+
+import test_oracle_attention as TA
+import test_oracle_rope as TR
+from oracle import attention as A
+from oracle import rope3d as R
+
+_orig_token_freqs = R.token_freqs
+_orig_positions = R.positions
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _mut_angles_dropped_two(d_b, theta):
+    j = np.arange(d_b // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -1.0 * j / d_b)
+
+
+def _mut_freqs_conj(tables, pos):
+    return np.conj(_orig_token_freqs(tables, pos))
+
+
+def _mut_freqs_band_order(tables, pos):
+    ft, fh, fw = tables
+    return np.concatenate([fh[pos[:, 1]], ft[pos[:, 0]], fw[pos[:, 2]]], axis=1)
+
+
+def _mut_positions_hw_swapped(F, H, W, s, off, n):
+    p = _orig_positions(F, H, W, s, off, n).copy()
+    i = np.arange(off, off + n) % (H * W)
+    p[:, 1], p[:, 2] = i % H, i // H
+    return p
+
+
+def _mut_positions_no_start(F, H, W, s, off, n):
+    p = _orig_positions(F, H, W, s, off, n).copy()
+    p[:, 0] -= s
+    return p
+
+
+def _mut_visible_strict(q_rows, q_pos, kv_len, C):
+    qc = (q_pos + np.asarray(q_rows)) // C
+    kc = np.arange(kv_len) // C
+    return kc[None, :] < qc[:, None]
+
+
+_orig_attn = A.chunk_causal_attention
+
+
+def _mut_attn_col_softmax(q, kc, vc, q_pos, kv_len, C, scale, rows=None, block=256):
+    q = np.asarray(q, dtype=np.float64)
+    b, lq, nh, d = q.shape
+    rows = np.arange(lq) if rows is None else np.asarray(rows)
+    out = np.empty((b, len(rows), nh, d))
+    for bi in range(b):
+        for h in range(nh):
+            s = scale * (q[bi, rows, h] @ kc[bi, :kv_len, h].T)
+            s = np.where(A.visible(rows, q_pos, kv_len, C), s, -np.inf)
+            p = np.exp(s - s.max(axis=0, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            out[bi, :, h] = p @ vc[bi, :kv_len, h]
+    return out
+
+
+def _mut_attn_no_scale(q, kc, vc, q_pos, kv_len, C, scale, rows=None, block=256):
+    return _orig_attn(q, kc, vc, q_pos, kv_len, C, 1.0, rows=rows, block=block)
+
+
+ROPE_PINS = [
+    (TR.test_rotation_matches_gptj_interleaved_rope_per_band, ((8, 8, 8),)),
+    (TR.test_unit_vector_closed_form, ()),
+    (TR.test_brute_force_rotation_loops_tiny, ()),
+    (TR.test_positions_brute_force_grid, (3, 5, 7, 9)),
+    (TR.test_start_frame_worked_example, ()),
+    (TR.test_shard_equals_unsharded_algorithm2, (8,)),
+]
+
+ATTN_PINS = [
+    (TA.test_brute_force_tiny, (64, 32, 96, 32)),
+    (TA.test_matches_torch_sdpa_fp64_with_bool_mask, ()),
+    (TA.test_closed_forms, ()),
+]
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("band_angles", _mut_angles_dropped_two),
+    ("token_freqs", _mut_freqs_conj),
+    ("token_freqs", _mut_freqs_band_order),
+    ("positions", _mut_positions_hw_swapped),
+    ("positions", _mut_positions_no_start),
+])
+def test_rope_mutant_is_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(R, attr, mutant)
+    assert any(_fails(fn, *args) for fn, args in ROPE_PINS), f"{mutant.__name__} survived"
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("visible", _mut_visible_strict),
+    ("chunk_causal_attention", _mut_attn_col_softmax),
+    ("chunk_causal_attention", _mut_attn_no_scale),
+])
+def test_attention_mutant_is_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(A, attr, mutant)
+    assert any(_fails(fn, *args) for fn, args in ATTN_PINS), f"{mutant.__name__} survived"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for fn, args in ROPE_PINS + ATTN_PINS:
+        assert not _fails(fn, *args), fn.__name__
