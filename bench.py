@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the Causal-RoPE + chunk-causal attention hot path on one MI355X.
+
+One step = one pass of the path over the Wan-1.3B-shaped 480P workload:
+rope3d_apply_append on the 4680-token chunk at global frames 6..8 (12 heads,
+head_dim 128, bf16) writing rotated K and V into the cache, then
+chunk_causal_attn of the chunk's 4680 queries over the 14040 cached keys
+(frames 0..8).  The cos/sin tables are built once per process before timing,
+as the method prescribes (precomputed, not per call).
+
+Prints ONE JSON line.  `value` is the step's attention TFLOP/s over the whole
+step time (RoPE included); the roofline object is for the dominant kernel
+(attention), timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunk-causal attn TFLOP/s + ms/chunk (Wan-1.3B 480P); RoPE kernel GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+N_SETS = 6  # rotating input sets: > 256 MB of traffic between reuses of one set
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=768,
+                   help="query rows per head in the oracle's timed sample")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn.hip", "rope3d.hip", "rcc_internal.h"):
+        with open(os.path.join(ROOT, "rope_chunk_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (this build has no multi-GPU path); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rope_chunk_causal_amd as rcc
+    from rope_chunk_causal_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rcc.lib()
+
+    wl = synth.WORKLOADS["480p_step"]
+    s = wl.start_frames[0]
+    nh, D, L, hw = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.hw
+    kv = (s + wl.frames) * hw
+    cap = kv
+    q_pos = s * hw
+    scale = 1.0 / math.sqrt(D)
+    r = wl.rope
+    cfg = rcc.rope_cfg(r.d_t, r.d_h, r.d_w, r.max_t, r.max_h, r.max_w, r.theta)
+
+    t0 = time.perf_counter()
+    tables = rcc.rope3d_tables(cfg)
+    torch.cuda.synchronize()
+    tables_ms = (time.perf_counter() - t0) * 1e3
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20)
+    bf = torch.bfloat16
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(bf)
+
+    sets = []
+    for _ in range(N_SETS):
+        sets.append(dict(
+            q=randn(1, L, nh, D), k=randn(1, L, nh, D), v=randn(1, L, nh, D),
+            q_out=torch.empty(1, L, nh, D, device=dev, dtype=bf),
+            kc=randn(1, cap, nh, D), vc=randn(1, cap, nh, D),   # frames 0..5 already cached
+            out=torch.empty(1, L, nh, D, device=dev, dtype=bf)))
+    grid = rcc.grid(wl.frames, wl.height, wl.width, s, 0)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        st = sets[i % N_SETS]
+        if ev is not None:
+            ev[0].record(stream)
+        rcc.rope3d_apply_append(cfg, tables, grid, st["q"], st["k"], st["v"], st["q_out"],
+                                st["kc"], st["vc"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        rcc.chunk_causal_attn(st["q_out"], st["kc"], st["vc"], st["out"], q_pos, kv, L, scale,
+                              stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-kernel durations with HIP events on the launch stream (separate pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    rope_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    attn_flops = 4.0 * L * kv * D * nh
+    rope_bytes = 6.0 * L * nh * D * 2
+    step_tflops = attn_flops / (ms_per_step * 1e-3) / 1e12
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    rope_gbps = rope_bytes / (rope_ms * 1e-3) / 1e9
+
+    # RoPE bandwidth configuration: one SP rank's 585-token slice, 64 chunks batched
+    sp = synth.WORKLOADS["480p_sp_shard"]
+    n_sp, B_sp, s_sp = sp.chunk_tokens // synth.SP_DEGREE, 64, sp.start_frames[0]
+    cap_sp = (s_sp + sp.frames) * sp.hw
+    sp_sets = []
+    for _ in range(2):
+        sp_sets.append([randn(B_sp, n_sp, nh, D) for _ in range(3)] +
+                       [torch.empty(B_sp, n_sp, nh, D, device=dev, dtype=bf),
+                        torch.empty(B_sp, cap_sp, nh, D, device=dev, dtype=bf),
+                        torch.empty(B_sp, cap_sp, nh, D, device=dev, dtype=bf)])
+    g_sp = rcc.grid(sp.frames, sp.height, sp.width, s_sp, 2 * n_sp)
+    for i in range(3):
+        rcc.rope3d_apply_append(cfg, tables, g_sp, *sp_sets[i % 2], stream=stream)
+    reps = 20
+    sp_ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    sp_ev[0].record(stream)
+    for i in range(reps):
+        rcc.rope3d_apply_append(cfg, tables, g_sp, *sp_sets[i % 2], stream=stream)
+        sp_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    sp_ms = sum(sp_ev[i].elapsed_time(sp_ev[i + 1]) for i in range(reps)) / reps
+    sp_bytes = 6.0 * B_sp * n_sp * nh * D * 2
+    sp_gbps = sp_bytes / (sp_ms * 1e-3) / 1e9
+
+    traffic = read_traffic("chunk_causal_attn_480p_step")
+    result = {
+        "metric": METRIC,
+        "value": round(step_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, Wan-1.3B 480P shapes)",
+        "config": {"workload": "480p_step", "heads": nh, "head_dim": D,
+                   "rope_bands": [r.d_t, r.d_h, r.d_w], "grid": [wl.frames, wl.height, wl.width],
+                   "start_frame": s, "q_tokens": L, "kv_tokens": kv, "batch": 1},
+        "ms_per_chunk": round(ms_per_step, 4),
+        "attn_ms": round(attn_ms, 4),
+        "attn_tflops": round(attn_tflops, 2),
+        "rope_ms": round(rope_ms, 4),
+        "rope_gbps": round(rope_gbps, 1),
+        "rope_sp_shard_b64": {"ms": round(sp_ms, 4), "gbps": round(sp_gbps, 1),
+                              "bytes": sp_bytes, "frac_hbm": round(sp_gbps / PEAK_HBM_GBPS, 4)},
+        "tables_once_ms": round(tables_ms, 3),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_rows, wl, s, kv, scale)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(rows_per_head, wl, s, kv, scale):
+    """The oracle (as it stands) timed on the host on a bounded sample of the step:
+    attention for `rows_per_head` query rows of every head, plus RoPE + append of
+    the same tokens.  Reported in the metric's unit (TFLOP/s of attention)."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import rope3d as R
+    from rope_chunk_causal_amd import synth
+
+    nh, D, L, hw = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.hw
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(L, size=rows_per_head, replace=False))
+    q = synth.to_f64(synth.normal((1, rows_per_head, nh, D), 22, "bf16"), "bf16")
+    k = synth.to_f64(synth.normal((1, rows_per_head, nh, D), 23, "bf16"), "bf16")
+    v = synth.to_f64(synth.normal((1, rows_per_head, nh, D), 24, "bf16"), "bf16")
+    kc = synth.to_f64(synth.normal((1, kv, nh, D), 25, "bf16"), "bf16")
+    vc = synth.to_f64(synth.normal((1, kv, nh, D), 26, "bf16"), "bf16")
+    r = wl.rope
+    t0 = time.perf_counter()
+    tabs = R.rope3d_tables(r.d_t, r.d_h, r.d_w, r.theta, r.max_t, r.max_h, r.max_w)
+    pos = R.positions(wl.frames, wl.height, wl.width, s, 0, L)[rows]
+    qr = R.rope3d_apply(q, tabs, pos)
+    kr = R.rope3d_apply(k, tabs, pos)
+    kc[:, pos[:, 3]] = kr
+    vc[:, pos[:, 3]] = v
+    t_rope = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    # the sampled queries sit at their own rows of the chunk (q_pos = s*HW)
+    qfull = np.zeros((1, L, nh, D))
+    qfull[:, rows] = qr
+    A.chunk_causal_attention(qfull, kc, vc, s * hw, kv, L, scale, rows=rows)
+    t_attn = time.perf_counter() - t0
+    flops = 4.0 * rows_per_head * kv * D * nh
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows_per_head} of {L} query rows per head x {nh} heads, Lk {kv}, fp64 "
+                      f"numpy: attention {t_attn:.2f} s; RoPE+append of the same tokens "
+                      f"{t_rope:.2f} s",
+            "attn_s": round(t_attn, 3), "rope_s": round(t_rope, 3),
+            "cpu": platform.processor() or platform.machine()}
+
+
+if __name__ == "__main__":
+    main()

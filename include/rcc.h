@@ -1,0 +1,178 @@
+/*
+ * rcc.h — C ABI of the Causal-RoPE + chunk-causal attention hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * [YL] C. Yuan, P. Li, "Accelerating Video Generation Inference with
+ *      Sequential-Parallel 3D Positional Encoding Using a Global Time
+ *      Index" (arXiv 2603.06664).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named *_dev / tensors are DEVICE pointers owned by the caller.
+ *   The library allocates no device memory and frees none.
+ * - Tensors are contiguous, row-major:
+ *     activations  [batch, tokens, n_heads, head_dim]
+ *     KV cache     [batch, cache_tokens, n_heads, head_dim]
+ *   Tokens of a chunk are flattened in row-major (frame, row, column)
+ *   order; cache row r holds the token whose index, counted over all
+ *   frames from global frame 0, is r.
+ * - Every tensor pointer must be 16-byte aligned (RCC_ERR_ALIGN).
+ * - Arguments are checked on the host before anything is launched; a call
+ *   that returns anything but RCC_OK has launched nothing and written
+ *   nothing.  Launches are asynchronous on `stream` (0 = the null stream);
+ *   a failed launch returns RCC_ERR_HIP.  No call synchronises the host.
+ * - rcc_last_error() returns a human-readable detail of the last non-OK
+ *   status returned on the calling thread.
+ */
+#ifndef RCC_H
+#define RCC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define RCC_API __attribute__((visibility("default")))
+#else
+#define RCC_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RCC_OK = 0,
+  RCC_ERR_NULL = 1,   /* a required pointer is NULL                         */
+  RCC_ERR_SHAPE = 2,  /* inconsistent or unsupported sizes                  */
+  RCC_ERR_RANGE = 3,  /* a position, token range or cache row out of range  */
+  RCC_ERR_DTYPE = 4,  /* unknown dtype code                                 */
+  RCC_ERR_ALIGN = 5,  /* a tensor pointer is not 16-byte aligned            */
+  RCC_ERR_HIP = 6     /* the HIP runtime reported an error                  */
+} rcc_status;
+
+typedef enum { RCC_F32 = 0, RCC_BF16 = 1 } rcc_dtype;
+
+/*
+ * RoPE band layout.  head_dim = d_t + d_h + d_w; each band dim is even and
+ * positive; the bands sit in t, h, w order along head_dim ([YL] §3.3.1:
+ * temporal, height and width frequency parts; Algorithm 2 concatenates the
+ * three per-axis tables in that order).  Band b, pair j (0 <= j < d_b/2)
+ * turns at theta^(-2j/d_b) radians per unit of that axis's coordinate.
+ * max_t/max_h/max_w are the table lengths: the largest global frame index,
+ * row and column + 1 that any later call may use.
+ */
+typedef struct {
+  int32_t d_t, d_h, d_w;
+  int32_t max_t, max_h, max_w;
+  double theta;
+} rcc_rope3d_cfg;
+
+/*
+ * Where a call's tokens sit.  frames/height/width: the chunk's grid
+ * (F = tau latent frames, H x W patches); start_frame: s = k * tau for
+ * chunk k ([YL] §3.3.2 item 1); token_offset: Delta, the index of the
+ * call's first token inside the chunk — r * L_local for sequence-parallel
+ * rank r ([YL] §3.3.3, Algorithm 3 step 2).
+ */
+typedef struct {
+  int32_t frames, height, width;
+  int32_t start_frame;
+  int64_t token_offset;
+} rcc_grid;
+
+/*
+ * Number of floats of the device table buffer for `cfg`, or -1 if cfg is
+ * NULL or invalid.  Layout (float2 = {cos, sin}):
+ *   [max_t][d_t/2] float2, then [max_h][d_h/2] float2, then [max_w][d_w/2].
+ */
+RCC_API int64_t rcc_rope3d_tables_floats(const rcc_rope3d_cfg* cfg);
+
+/*
+ * rope3d_tables — fill `tables_dev` (rcc_rope3d_tables_floats(cfg) floats,
+ * caller-owned) with cos/sin of p * theta_{b,j} for every axis b, position
+ * p < max_b and pair j.  Angles and cos/sin are evaluated in fp64 on the
+ * device and stored rounded to fp32.  Done once; later calls only read it
+ * ([YL] §3.4.1 item 2: cos/sin precomputed into contiguous memory instead
+ * of per-call caching; Algorithm 2's `freqs`).
+ * Errors: NULL, SHAPE (odd or non-positive band dim, non-positive length,
+ * theta <= 0), ALIGN, HIP.
+ */
+RCC_API rcc_status rcc_rope3d_tables(const rcc_rope3d_cfg* cfg, float* tables_dev,
+                             hipStream_t stream);
+
+/*
+ * rope3d_positions — write int32 [n_tokens][4] = {t_global, h, w,
+ * cache_row} for the call's tokens, computed by the same device function
+ * the RoPE kernel uses ([YL] §3.3.3 and Algorithm 3 step 3:
+ * i_global = Delta + i, t_global = s + floor(i_global / (H*W)); h and w in
+ * row-major order; cache_row = s*H*W + i_global).  A check/debug export.
+ * Errors: NULL, SHAPE (non-positive grid), RANGE (Delta < 0, Delta + n >
+ * F*H*W, a cache row >= 2^31), ALIGN, HIP.
+ */
+RCC_API rcc_status rcc_rope3d_positions(const rcc_grid* grid, int64_t n_tokens,
+                                int32_t* thw_dev, hipStream_t stream);
+
+/*
+ * rope3d_apply_append — Causal-RoPE SP on one token range, fused with the
+ * KV-cache write ([YL] Algorithm 3 steps 2, 3 and 5; rotation of
+ * Algorithm 2 and the §3.3.2 item 2 equation).
+ *   q, k, v   [batch, n_tokens, n_heads, D] in `in_dtype`
+ *   q_out     [batch, n_tokens, n_heads, D] in `out_dtype`; may equal q
+ *             when the dtypes match.
+ *   k_cache, v_cache [batch, cache_tokens, n_heads, D] in `out_dtype`.
+ * Per token at (t, h, w) and pair j of band b, (x_2j + i x_2j+1) is
+ * multiplied by cos + i sin of that band's table at that axis's
+ * coordinate (fp32 arithmetic).  q_out gets rotated q; cache rows
+ * s*H*W + Delta + [0, n_tokens) get rotated k and the unrotated v
+ * (overwriting them); no other cache row is touched.
+ * Errors: NULL; DTYPE; SHAPE (D != d_t + d_h + d_w, D % 8 != 0, batch,
+ * n_heads or grid non-positive, n_tokens < 0); RANGE (Delta < 0,
+ * Delta + n_tokens > F*H*W, s < 0, s + F > max_t, H > max_h, W > max_w,
+ * s*H*W + Delta + n_tokens > cache_tokens); ALIGN; HIP.
+ */
+RCC_API rcc_status rcc_rope3d_apply_append(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int64_t n_tokens, int32_t n_heads,
+    const void* q, const void* k, const void* v,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream);
+
+/*
+ * chunk_causal_attn — attention of a query chunk over the KV cache
+ * ([YL] Algorithm 3 step 6, with the causal consistency across blocks of
+ * §3.2 read as block (chunk) causal visibility).
+ *   q        [batch, q_tokens, n_heads, head_dim] in `in_dtype`; query row
+ *            i sits at cache position q_pos + i.
+ *   k_cache, v_cache [batch, cache_tokens, n_heads, head_dim] in `in_dtype`.
+ *   out      [batch, q_tokens, n_heads, head_dim] in `out_dtype`.
+ * Key j is visible to query i iff j < kv_tokens and
+ * floor(j / chunk_tokens) <= floor((q_pos + i) / chunk_tokens).
+ * out = softmax(scale * q k^T over visible keys) v.  Operands are rounded
+ * to bf16 (nearest-even) for the matrix cores; accumulation and softmax
+ * state are fp32.
+ * Errors: NULL; DTYPE; SHAPE (head_dim not a multiple of 8 in [8, 128],
+ * batch/n_heads/chunk_tokens non-positive, q_tokens < 0); RANGE
+ * (q_pos < 0, q_pos + q_tokens > kv_tokens, kv_tokens > cache_tokens,
+ * sizes >= 2^31); ALIGN; HIP.
+ */
+RCC_API rcc_status rcc_chunk_causal_attn(
+    rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int32_t n_heads, int32_t head_dim,
+    int64_t q_tokens, int64_t q_pos, int64_t kv_tokens, int64_t chunk_tokens,
+    float scale,
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
+    void* out, hipStream_t stream);
+
+/* Static string naming a status code. */
+RCC_API const char* rcc_status_string(rcc_status s);
+
+/* Detail of the last non-OK status on this thread ("" if none). */
+RCC_API const char* rcc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RCC_H */

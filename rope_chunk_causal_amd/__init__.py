@@ -1,0 +1,211 @@
+"""Thin ctypes binding over librcc.so (include/rcc.h), same names as the C ABI.
+
+Argument marshalling only: every step of the path runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  The
+binding checks that each tensor is contiguous, on the GPU, of a supported
+dtype and large enough for the sizes passed, so the kernels never address
+memory outside the caller's tensors; everything else is checked in C.
+
+If librcc.so is missing or does not load, ``lib()`` raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "librcc.so")
+
+RCC_OK, RCC_ERR_NULL, RCC_ERR_SHAPE, RCC_ERR_RANGE, RCC_ERR_DTYPE, RCC_ERR_ALIGN, RCC_ERR_HIP = range(7)
+RCC_F32, RCC_BF16 = 0, 1
+
+EXPORTS = ("rcc_rope3d_tables_floats", "rcc_rope3d_tables", "rcc_rope3d_positions",
+           "rcc_rope3d_apply_append", "rcc_chunk_causal_attn", "rcc_status_string",
+           "rcc_last_error")
+
+
+class RccError(RuntimeError):
+    def __init__(self, status: int, call: str, detail: str):
+        self.status = status
+        super().__init__(f"{call}: {_status_name(status)}: {detail}")
+
+
+class rcc_rope3d_cfg(ctypes.Structure):
+    _fields_ = [("d_t", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_w", ctypes.c_int32),
+                ("max_t", ctypes.c_int32), ("max_h", ctypes.c_int32), ("max_w", ctypes.c_int32),
+                ("theta", ctypes.c_double)]
+
+
+class rcc_grid(ctypes.Structure):
+    _fields_ = [("frames", ctypes.c_int32), ("height", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("start_frame", ctypes.c_int32),
+                ("token_offset", ctypes.c_int64)]
+
+
+def rope_cfg(d_t, d_h, d_w, max_t, max_h, max_w, theta=10000.0) -> rcc_rope3d_cfg:
+    return rcc_rope3d_cfg(d_t, d_h, d_w, max_t, max_h, max_w, float(theta))
+
+
+def grid(frames, height, width, start_frame, token_offset=0) -> rcc_grid:
+    return rcc_grid(frames, height, width, start_frame, token_offset)
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librcc.so once; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m rope_chunk_causal_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+    cfgp, gridp = ctypes.POINTER(rcc_rope3d_cfg), ctypes.POINTER(rcc_grid)
+    L.rcc_rope3d_tables_floats.argtypes = [cfgp]
+    L.rcc_rope3d_tables_floats.restype = I64
+    L.rcc_rope3d_tables.argtypes = [cfgp, P, P]
+    L.rcc_rope3d_tables.restype = ctypes.c_int
+    L.rcc_rope3d_positions.argtypes = [gridp, I64, P, P]
+    L.rcc_rope3d_positions.restype = ctypes.c_int
+    L.rcc_rope3d_apply_append.argtypes = [cfgp, P, gridp, ctypes.c_int, ctypes.c_int,
+                                          I32, I64, I32, P, P, P, P, P, P, I64, P]
+    L.rcc_rope3d_apply_append.restype = ctypes.c_int
+    L.rcc_chunk_causal_attn.argtypes = [ctypes.c_int, ctypes.c_int, I32, I32, I32,
+                                        I64, I64, I64, I64, F, P, P, P, I64, P, P]
+    L.rcc_chunk_causal_attn.restype = ctypes.c_int
+    L.rcc_status_string.argtypes = [ctypes.c_int]
+    L.rcc_status_string.restype = ctypes.c_char_p
+    L.rcc_last_error.argtypes = []
+    L.rcc_last_error.restype = ctypes.c_char_p
+    _ = D
+    _lib = L
+    return L
+
+
+def _status_name(st: int) -> str:
+    try:
+        return lib().rcc_status_string(st).decode()
+    except Exception:  # pragma: no cover
+        return str(st)
+
+
+def _check(st: int, call: str) -> None:
+    if st != RCC_OK:
+        raise RccError(st, call, lib().rcc_last_error().decode())
+
+
+# ---------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RCC_F32
+    if t.dtype == torch.bfloat16:
+        return RCC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t, name: str, numel: int, dtype=None) -> int:
+    """data_ptr of a contiguous GPU tensor holding at least `numel` elements."""
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ----------------------------------------------------------- entry points
+
+def rope3d_tables_floats(cfg: rcc_rope3d_cfg) -> int:
+    n = lib().rcc_rope3d_tables_floats(ctypes.byref(cfg))
+    if n < 0:
+        raise RccError(RCC_ERR_SHAPE, "rope3d_tables_floats", "invalid cfg")
+    return n
+
+
+def rope3d_tables(cfg: rcc_rope3d_cfg, tables=None, stream=None):
+    """Fill (or allocate and fill) the fp32 cos/sin table buffer on the GPU."""
+    torch = _torch()
+    n = rope3d_tables_floats(cfg)
+    if tables is None:
+        tables = torch.empty(n, dtype=torch.float32, device="cuda")
+    _check(lib().rcc_rope3d_tables(ctypes.byref(cfg), _ptr(tables, "tables", n, torch.float32),
+                                   _stream(stream)), "rope3d_tables")
+    return tables
+
+
+def rope3d_positions(g: rcc_grid, n_tokens: int, thw=None, stream=None):
+    """int32 [n_tokens, 4] = (t_global, h, w, cache_row) from the device function."""
+    torch = _torch()
+    if thw is None:
+        thw = torch.empty((max(n_tokens, 0), 4), dtype=torch.int32, device="cuda")
+    p = _ptr(thw, "thw", 4 * max(n_tokens, 0), torch.int32) if n_tokens > 0 else 0
+    _check(lib().rcc_rope3d_positions(ctypes.byref(g), n_tokens, p, _stream(stream)),
+           "rope3d_positions")
+    return thw
+
+
+def rope3d_apply_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, q, k, v, q_out,
+                        k_cache, v_cache, stream=None) -> None:
+    """q, k, v [B, n, heads, D]; q_out same shape; caches [B, cache_tokens, heads, D]."""
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or q_out.shape != q.shape:
+        raise ValueError("q, k, v, q_out must share one [B, n, heads, D] shape")
+    B, n, nh, D = q.shape
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or \
+            k_cache.shape[0] != B or tuple(k_cache.shape[2:]) != (nh, D):
+        raise ValueError("caches must be [B, cache_tokens, heads, D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or k_cache.dtype != q_out.dtype or \
+            v_cache.dtype != q_out.dtype:
+        raise TypeError("q/k/v share in_dtype; q_out/k_cache/v_cache share out_dtype")
+    cap = k_cache.shape[1]
+    numel = B * n * nh * D
+    ntab = rope3d_tables_floats(cfg)
+    _check(lib().rcc_rope3d_apply_append(
+        ctypes.byref(cfg), _ptr(tables, "tables", ntab, torch.float32), ctypes.byref(g),
+        _dtype_code(q), _dtype_code(q_out), B, n, nh,
+        _ptr(q, "q", numel), _ptr(k, "k", numel), _ptr(v, "v", numel),
+        _ptr(q_out, "q_out", numel), _ptr(k_cache, "k_cache", B * cap * nh * D),
+        _ptr(v_cache, "v_cache", B * cap * nh * D), cap, _stream(stream)),
+        "rope3d_apply_append")
+
+
+def chunk_causal_attn(q, k_cache, v_cache, out, q_pos: int, kv_tokens: int,
+                      chunk_tokens: int, scale: float, stream=None) -> None:
+    """q [B, Lq, heads, D], caches [B, cache_tokens, heads, D], out like q."""
+    if q.dim() != 4 or out.shape != q.shape:
+        raise ValueError("q and out must share one [B, Lq, heads, D] shape")
+    B, lq, nh, D = q.shape
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or \
+            k_cache.shape[0] != B or tuple(k_cache.shape[2:]) != (nh, D):
+        raise ValueError("caches must be [B, cache_tokens, heads, D]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches share in_dtype")
+    cap = k_cache.shape[1]
+    _check(lib().rcc_chunk_causal_attn(
+        _dtype_code(q), _dtype_code(out), B, nh, D, lq, q_pos, kv_tokens, chunk_tokens,
+        float(scale), _ptr(q, "q", B * lq * nh * D), _ptr(k_cache, "k_cache", B * cap * nh * D),
+        _ptr(v_cache, "v_cache", B * cap * nh * D), cap, _ptr(out, "out", B * lq * nh * D),
+        _stream(stream)), "chunk_causal_attn")

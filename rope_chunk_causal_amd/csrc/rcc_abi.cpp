@@ -1,0 +1,223 @@
+// C ABI: argument checks, then asynchronous launches on the caller's stream.
+// Every check runs before any launch, so a non-OK return has touched no
+// memory.  See include/rcc.h for the contract of each entry point.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "rcc_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rcc_status fail(rcc_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+rcc_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RCC_OK;
+  return fail(RCC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool valid_dtype(rcc_dtype d) { return d == RCC_F32 || d == RCC_BF16; }
+constexpr int64_t kI32Max = 2147483647;
+
+rcc_status check_cfg(const rcc_rope3d_cfg* c) {
+  if (!c) return fail(RCC_ERR_NULL, "cfg is NULL");
+  if (c->d_t <= 0 || c->d_h <= 0 || c->d_w <= 0 || (c->d_t | c->d_h | c->d_w) & 1)
+    return fail(RCC_ERR_SHAPE, "band dims must be even and positive (got %d/%d/%d)",
+                c->d_t, c->d_h, c->d_w);
+  if (c->max_t <= 0 || c->max_h <= 0 || c->max_w <= 0)
+    return fail(RCC_ERR_SHAPE, "table lengths must be positive");
+  if (!(c->theta > 0.0) || !isfinite(c->theta))
+    return fail(RCC_ERR_SHAPE, "theta must be positive and finite");
+  return RCC_OK;
+}
+
+// Grid + token range checks shared by positions and apply_append.
+rcc_status check_grid(const rcc_grid* g, int64_t n_tokens, rcc::GridArgs* out) {
+  if (!g) return fail(RCC_ERR_NULL, "grid is NULL");
+  if (g->frames <= 0 || g->height <= 0 || g->width <= 0)
+    return fail(RCC_ERR_SHAPE, "grid dims must be positive");
+  const int64_t hw = (int64_t)g->height * g->width;
+  const int64_t L = hw * g->frames;
+  if (L > kI32Max) return fail(RCC_ERR_SHAPE, "F*H*W must be < 2^31");
+  if (n_tokens < 0) return fail(RCC_ERR_SHAPE, "n_tokens < 0");
+  if (g->start_frame < 0) return fail(RCC_ERR_RANGE, "start_frame < 0");
+  if (g->token_offset < 0 || g->token_offset + n_tokens > L)
+    return fail(RCC_ERR_RANGE, "token range [%lld, %lld) outside the chunk of %lld tokens",
+                (long long)g->token_offset, (long long)(g->token_offset + n_tokens),
+                (long long)L);
+  if ((int64_t)g->start_frame * hw + g->token_offset + n_tokens > kI32Max)
+    return fail(RCC_ERR_RANGE, "cache rows must be < 2^31");
+  out->height = g->height;
+  out->width = g->width;
+  out->hw = (int32_t)hw;
+  out->start_frame = g->start_frame;
+  out->token_offset = (int32_t)g->token_offset;
+  return RCC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rcc_status_string(rcc_status s) {
+  switch (s) {
+    case RCC_OK: return "RCC_OK";
+    case RCC_ERR_NULL: return "RCC_ERR_NULL";
+    case RCC_ERR_SHAPE: return "RCC_ERR_SHAPE";
+    case RCC_ERR_RANGE: return "RCC_ERR_RANGE";
+    case RCC_ERR_DTYPE: return "RCC_ERR_DTYPE";
+    case RCC_ERR_ALIGN: return "RCC_ERR_ALIGN";
+    case RCC_ERR_HIP: return "RCC_ERR_HIP";
+  }
+  return "RCC_ERR_UNKNOWN";
+}
+
+const char* rcc_last_error(void) { return g_last_error; }
+
+int64_t rcc_rope3d_tables_floats(const rcc_rope3d_cfg* cfg) {
+  if (check_cfg(cfg) != RCC_OK) return -1;
+  return (int64_t)cfg->max_t * cfg->d_t + (int64_t)cfg->max_h * cfg->d_h +
+         (int64_t)cfg->max_w * cfg->d_w;
+}
+
+rcc_status rcc_rope3d_tables(const rcc_rope3d_cfg* cfg, float* tables_dev,
+                             hipStream_t stream) {
+  rcc_status st = check_cfg(cfg);
+  if (st != RCC_OK) return st;
+  if (!tables_dev) return fail(RCC_ERR_NULL, "tables_dev is NULL");
+  if (!aligned16(tables_dev)) return fail(RCC_ERR_ALIGN, "tables_dev not 16-byte aligned");
+  return from_hip(rcc::launch_rope3d_tables(*cfg, tables_dev, stream), "rope3d_tables launch");
+}
+
+rcc_status rcc_rope3d_positions(const rcc_grid* grid, int64_t n_tokens, int32_t* thw_dev,
+                                hipStream_t stream) {
+  rcc::GridArgs g;
+  rcc_status st = check_grid(grid, n_tokens, &g);
+  if (st != RCC_OK) return st;
+  if (n_tokens == 0) return RCC_OK;
+  if (!thw_dev) return fail(RCC_ERR_NULL, "thw_dev is NULL");
+  if (!aligned16(thw_dev)) return fail(RCC_ERR_ALIGN, "thw_dev not 16-byte aligned");
+  return from_hip(rcc::launch_rope3d_positions(g, (int32_t)n_tokens, thw_dev, stream),
+                  "rope3d_positions launch");
+}
+
+rcc_status rcc_rope3d_apply_append(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int64_t n_tokens, int32_t n_heads,
+    const void* q, const void* k, const void* v,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream) {
+  rcc_status st = check_cfg(cfg);
+  if (st != RCC_OK) return st;
+  rcc::GridArgs g;
+  st = check_grid(grid, n_tokens, &g);
+  if (st != RCC_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(RCC_ERR_DTYPE, "unknown dtype code");
+  const int64_t D = (int64_t)cfg->d_t + cfg->d_h + cfg->d_w;
+  if (D % 8) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 8", (long long)D);
+  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
+  if ((int64_t)n_heads * D > kI32Max || n_tokens * (D / 8) > kI32Max)
+    return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
+  if ((int64_t)grid->start_frame + grid->frames > cfg->max_t)
+    return fail(RCC_ERR_RANGE, "frames [%d, %d) exceed the time table (max_t %d)",
+                grid->start_frame, grid->start_frame + grid->frames, cfg->max_t);
+  if (grid->height > cfg->max_h || grid->width > cfg->max_w)
+    return fail(RCC_ERR_RANGE, "grid %dx%d exceeds the h/w tables (%d, %d)",
+                grid->height, grid->width, cfg->max_h, cfg->max_w);
+  const int64_t last_row = (int64_t)grid->start_frame * g.hw + grid->token_offset + n_tokens;
+  if (last_row > cache_tokens)
+    return fail(RCC_ERR_RANGE, "cache rows up to %lld exceed cache_tokens %lld",
+                (long long)last_row, (long long)cache_tokens);
+  if (n_tokens == 0) return RCC_OK;
+  if (!tables_dev || !q || !k || !v || !q_out || !k_cache || !v_cache)
+    return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
+  if (!aligned16(tables_dev) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (q_out == (const void*)q && in_dtype != out_dtype)
+    return fail(RCC_ERR_DTYPE, "in-place q_out needs in_dtype == out_dtype");
+
+  rcc::RopeArgs a;
+  a.tables = tables_dev;
+  a.pt = cfg->d_t / 2;
+  a.ph = cfg->d_h / 2;
+  a.pw = cfg->d_w / 2;
+  a.off_h = (int64_t)cfg->max_t * a.pt;
+  a.off_w = a.off_h + (int64_t)cfg->max_h * a.ph;
+  a.grid = g;
+  a.batch = batch;
+  a.n_tokens = (int32_t)n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = (int32_t)D;
+  a.cache_tokens = cache_tokens;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return from_hip(rcc::launch_rope3d_apply_append(a, in_dtype, out_dtype, stream),
+                  "rope3d_apply_append launch");
+}
+
+rcc_status rcc_chunk_causal_attn(
+    rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int32_t n_heads, int32_t head_dim,
+    int64_t q_tokens, int64_t q_pos, int64_t kv_tokens, int64_t chunk_tokens,
+    float scale,
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
+    void* out, hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(RCC_ERR_DTYPE, "unknown dtype code");
+  if (head_dim < 8 || head_dim > 128 || head_dim % 8)
+    return fail(RCC_ERR_SHAPE, "head_dim must be a multiple of 8 in [8, 128] (got %d)", head_dim);
+  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (n_heads <= 0 || n_heads > 65535) return fail(RCC_ERR_SHAPE, "n_heads must be in [1, 65535]");
+  if (chunk_tokens <= 0) return fail(RCC_ERR_SHAPE, "chunk_tokens must be positive");
+  if (q_tokens < 0) return fail(RCC_ERR_SHAPE, "q_tokens < 0");
+  if (!isfinite(scale)) return fail(RCC_ERR_SHAPE, "scale must be finite");
+  if (q_pos < 0 || q_pos + q_tokens > kv_tokens)
+    return fail(RCC_ERR_RANGE, "query rows [%lld, %lld) not inside the %lld visible keys",
+                (long long)q_pos, (long long)(q_pos + q_tokens), (long long)kv_tokens);
+  if (kv_tokens > cache_tokens)
+    return fail(RCC_ERR_RANGE, "kv_tokens %lld > cache_tokens %lld", (long long)kv_tokens,
+                (long long)cache_tokens);
+  if (kv_tokens + chunk_tokens > kI32Max || (int64_t)n_heads * head_dim > kI32Max)
+    return fail(RCC_ERR_RANGE, "sizes must be < 2^31");
+  if (q_tokens == 0) return RCC_OK;
+  if (!q || !k_cache || !v_cache || !out) return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+
+  rcc::AttnArgs a;
+  a.batch = batch;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.q_tokens = (int32_t)q_tokens;
+  a.q_pos = (int32_t)q_pos;
+  a.kv_tokens = (int32_t)kv_tokens;
+  a.chunk_tokens = (int32_t)chunk_tokens;
+  a.cache_tokens = cache_tokens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  return from_hip(rcc::launch_chunk_causal_attn(a, in_dtype, out_dtype, stream),
+                  "chunk_causal_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal declarations shared by the kernel files and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rcc.h"
+
+namespace rcc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Position of a call's token inside the video ([YL] §3.3.3).  All values
+// fit in 32 bits: the host checks F*H*W < 2^31 and cache rows < 2^31.
+struct GridArgs {
+  int32_t height, width, hw;  // H, W, H*W
+  int32_t start_frame;        // s
+  int32_t token_offset;       // Delta
+};
+
+struct TokenPos {
+  int32_t t, h, w, row;
+};
+
+// i_global = Delta + i; frame in chunk = i_global / HW; t_global = s + frame;
+// h, w in row-major order; cache row = s*HW + i_global.
+__device__ __forceinline__ TokenPos token_position(const GridArgs& g, int32_t i) {
+  const uint32_t ig = (uint32_t)(g.token_offset + i);
+  const uint32_t f = ig / (uint32_t)g.hw;
+  const uint32_t rem = ig - f * (uint32_t)g.hw;
+  const uint32_t h = rem / (uint32_t)g.width;
+  TokenPos p;
+  p.t = g.start_frame + (int32_t)f;
+  p.h = (int32_t)h;
+  p.w = (int32_t)(rem - h * (uint32_t)g.width);
+  p.row = g.start_frame * g.hw + (int32_t)ig;
+  return p;
+}
+
+// Launchers (argument checks are done by the C-ABI layer before these run).
+hipError_t launch_rope3d_tables(const rcc_rope3d_cfg& cfg, float* tables, hipStream_t s);
+hipError_t launch_rope3d_positions(const GridArgs& g, int32_t n, int32_t* thw, hipStream_t s);
+
+struct RopeArgs {
+  const float* tables;
+  int32_t pt, ph, pw;         // pairs per band
+  int64_t off_h, off_w;       // float2 offsets of the h and w tables
+  GridArgs grid;
+  int32_t batch, n_tokens, n_heads, head_dim;
+  int64_t cache_tokens;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+};
+hipError_t launch_rope3d_apply_append(const RopeArgs& a, rcc_dtype in, rcc_dtype out,
+                                      hipStream_t s);
+
+struct AttnArgs {
+  int32_t batch, n_heads, head_dim;
+  int32_t q_tokens, q_pos, kv_tokens, chunk_tokens;
+  int64_t cache_tokens;
+  float scale_log2;           // scale * log2(e)
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+};
+hipError_t launch_chunk_causal_attn(const AttnArgs& a, rcc_dtype in, rcc_dtype out,
+                                    hipStream_t s);
+
+}  // namespace rcc

@@ -1,0 +1,245 @@
+// 3D RoPE with a global time index, fused with the KV-cache write, for gfx950.
+//
+// [YL] Yuan & Li, "Accelerating Video Generation Inference with
+// Sequential-Parallel 3D Positional Encoding Using a Global Time Index":
+//   tables        §3.4.1 item 2 and Algorithm 2 (`freqs`, one per axis)
+//   positions     §3.3.2 item 1, §3.3.3, Algorithm 3 steps 2-3
+//   rotation      §3.3.1 equation, §3.3.2 item 2, Algorithm 2 (adjacent pairs
+//                 viewed as complex numbers, multiplied by cos + i sin)
+//   cache write   Algorithm 3 step 5
+//
+// The apply kernel is HBM-bound: per token it reads q, k, v and writes
+// q', k-cache and v-cache rows (6 * n_heads * D elements).  One thread owns
+// 8 consecutive elements (4 rotary pairs) of a token's head vector; it
+// fetches the 4 (cos, sin) pairs of its slot once from the L2-resident
+// tables and reuses them for HEADS_PER_THREAD heads of q and k, so the
+// table traffic is a small fraction of the streamed bytes.  All loads of a
+// thread are issued before its first store (bytes in flight, and in-place
+// q_out == q stays correct).
+#include "rcc_internal.h"
+
+namespace rcc {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kHeadsPerThread = 4;
+
+// ---------------------------------------------------------------- tables
+
+__global__ __launch_bounds__(kBlock) void rope3d_tables_kernel(
+    float2* __restrict__ out, double theta, int32_t pt, int32_t ph, int32_t pw,
+    int32_t max_t, int32_t max_h, int32_t max_w) {
+  const int64_t nt = (int64_t)max_t * pt, nh = (int64_t)max_h * ph,
+                nw = (int64_t)max_w * pw;
+  const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (idx >= nt + nh + nw) return;
+  int64_t r = idx;
+  int32_t pairs;
+  if (r < nt) {
+    pairs = pt;
+  } else if (r < nt + nh) {
+    r -= nt;
+    pairs = ph;
+  } else {
+    r -= nt + nh;
+    pairs = pw;
+  }
+  const int64_t p = r / pairs;
+  const int32_t j = (int32_t)(r - p * pairs);
+  // theta_{b,j} = theta^(-2j/d_b), d_b = 2 * pairs; evaluated in fp64.
+  const double freq = pow(theta, -(2.0 * (double)j) / (double)(2 * pairs));
+  const double ang = (double)p * freq;
+  double s, c;
+  sincos(ang, &s, &c);
+  out[idx] = make_float2((float)c, (float)s);
+}
+
+// ------------------------------------------------------------- positions
+
+__global__ __launch_bounds__(kBlock) void rope3d_positions_kernel(
+    GridArgs g, int32_t n, int4* __restrict__ out) {
+  const int32_t i = blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const TokenPos p = token_position(g, i);
+  out[i] = make_int4(p.t, p.h, p.w, p.row);
+}
+
+// ----------------------------------------------------------------- apply
+
+template <typename T> struct Vec8;
+
+template <> struct Vec8<__bf16> {
+  uint4 raw;
+  __device__ __forceinline__ void load(const __bf16* p) {
+    raw = *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ __forceinline__ void to_float(float f[8]) const {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <> struct Vec8<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = reinterpret_cast<const float4*>(p)[0];
+    hi = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void to_float(float f[8]) const {
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  }
+};
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32) and 16-byte store.
+__device__ __forceinline__ void store8(__bf16* p, const float f[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)f[i];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+
+__device__ __forceinline__ void store8(float* p, const float f[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// Same-type copy of v is a bit copy; otherwise it goes through fp32.
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void copy8(Tout* dst, const Vec8<Tin>& v) {
+  float f[8];
+  v.to_float(f);
+  store8(dst, f);
+}
+template <>
+__device__ __forceinline__ void copy8<__bf16, __bf16>(__bf16* dst, const Vec8<__bf16>& v) {
+  *reinterpret_cast<uint4*>(dst) = v.raw;
+}
+template <>
+__device__ __forceinline__ void copy8<float, float>(float* dst, const Vec8<float>& v) {
+  reinterpret_cast<float4*>(dst)[0] = v.lo;
+  reinterpret_cast<float4*>(dst)[1] = v.hi;
+}
+
+// (x0 + i x1) * (c + i s) for 4 pairs.
+__device__ __forceinline__ void rotate8(float x[8], const float c[4], const float s[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float x0 = x[2 * q], x1 = x[2 * q + 1];
+    x[2 * q] = x0 * c[q] - x1 * s[q];
+    x[2 * q + 1] = x0 * s[q] + x1 * c[q];
+  }
+}
+
+// grid: x = ceil(n_tokens * D/8 / kBlock), y = head groups, z = batch.
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(kBlock) void rope3d_apply_append_kernel(RopeArgs a) {
+  const int32_t slots = a.head_dim >> 3;                       // 8-element slots per head
+  const uint32_t tid = blockIdx.x * kBlock + threadIdx.x;
+  if (tid >= (uint32_t)a.n_tokens * (uint32_t)slots) return;
+  const int32_t i = (int32_t)(tid / (uint32_t)slots);
+  const int32_t c = (int32_t)(tid - (uint32_t)i * (uint32_t)slots);
+  const int32_t b = blockIdx.z;
+  const TokenPos p = token_position(a.grid, i);
+
+  // cos/sin of the 4 pairs of this slot; each pair reads its own band's table.
+  const float2* tab = reinterpret_cast<const float2*>(a.tables);
+  float cs[4], sn[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int32_t j = 4 * c + q;
+    const float2* src;
+    if (j < a.pt) {
+      src = tab + (int64_t)p.t * a.pt + j;
+    } else if (j < a.pt + a.ph) {
+      src = tab + a.off_h + (int64_t)p.h * a.ph + (j - a.pt);
+    } else {
+      src = tab + a.off_w + (int64_t)p.w * a.pw + (j - a.pt - a.ph);
+    }
+    const float2 v = *src;
+    cs[q] = v.x;
+    sn[q] = v.y;
+  }
+
+  const int64_t row_stride = (int64_t)a.n_heads * a.head_dim;
+  const int64_t in_base = ((int64_t)b * a.n_tokens + i) * row_stride + 8 * c;
+  const int64_t cache_base = ((int64_t)b * a.cache_tokens + p.row) * row_stride + 8 * c;
+  const Tin* q = reinterpret_cast<const Tin*>(a.q) + in_base;
+  const Tin* k = reinterpret_cast<const Tin*>(a.k) + in_base;
+  const Tin* v = reinterpret_cast<const Tin*>(a.v) + in_base;
+  Tout* qo = reinterpret_cast<Tout*>(a.q_out) + in_base;
+  Tout* kc = reinterpret_cast<Tout*>(a.k_cache) + cache_base;
+  Tout* vc = reinterpret_cast<Tout*>(a.v_cache) + cache_base;
+
+  const int32_t h0 = blockIdx.y * kHeadsPerThread;
+  Vec8<Tin> vq[kHeadsPerThread], vk[kHeadsPerThread], vv[kHeadsPerThread];
+#pragma unroll
+  for (int hh = 0; hh < kHeadsPerThread; ++hh) {
+    if (h0 + hh < a.n_heads) {
+      const int64_t o = (int64_t)(h0 + hh) * a.head_dim;
+      vq[hh].load(q + o);
+      vk[hh].load(k + o);
+      vv[hh].load(v + o);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < kHeadsPerThread; ++hh) {
+    if (h0 + hh < a.n_heads) {
+      const int64_t o = (int64_t)(h0 + hh) * a.head_dim;
+      float x[8];
+      vq[hh].to_float(x);
+      rotate8(x, cs, sn);
+      store8(qo + o, x);
+      vk[hh].to_float(x);
+      rotate8(x, cs, sn);
+      store8(kc + o, x);
+      copy8<Tin, Tout>(vc + o, vv[hh]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope3d_tables(const rcc_rope3d_cfg& cfg, float* tables, hipStream_t s) {
+  const int32_t pt = cfg.d_t / 2, ph = cfg.d_h / 2, pw = cfg.d_w / 2;
+  const int64_t total = (int64_t)cfg.max_t * pt + (int64_t)cfg.max_h * ph +
+                        (int64_t)cfg.max_w * pw;
+  const uint32_t blocks = (uint32_t)((total + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL(rope3d_tables_kernel, dim3(blocks), dim3(kBlock), 0, s,
+                     reinterpret_cast<float2*>(tables), cfg.theta, pt, ph, pw,
+                     cfg.max_t, cfg.max_h, cfg.max_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope3d_positions(const GridArgs& g, int32_t n, int32_t* thw, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const uint32_t blocks = (uint32_t)((n + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL(rope3d_positions_kernel, dim3(blocks), dim3(kBlock), 0, s, g, n,
+                     reinterpret_cast<int4*>(thw));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope3d_apply_append(const RopeArgs& a, rcc_dtype in, rcc_dtype out,
+                                      hipStream_t s) {
+  if (a.n_tokens == 0) return hipSuccess;
+  const int64_t threads = (int64_t)a.n_tokens * (a.head_dim / 8);
+  const dim3 grid((uint32_t)((threads + kBlock - 1) / kBlock),
+                  (uint32_t)((a.n_heads + kHeadsPerThread - 1) / kHeadsPerThread),
+                  (uint32_t)a.batch);
+  if (in == RCC_BF16 && out == RCC_BF16)
+    hipLaunchKernelGGL((rope3d_apply_append_kernel<__bf16, __bf16>), grid, dim3(kBlock), 0, s, a);
+  else if (in == RCC_BF16 && out == RCC_F32)
+    hipLaunchKernelGGL((rope3d_apply_append_kernel<__bf16, float>), grid, dim3(kBlock), 0, s, a);
+  else if (in == RCC_F32 && out == RCC_BF16)
+    hipLaunchKernelGGL((rope3d_apply_append_kernel<float, __bf16>), grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((rope3d_apply_append_kernel<float, float>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace rcc

@@ -1,0 +1,87 @@
+"""Helpers shared by the GPU parity tests: device transfer of seeded inputs,
+bf16 views for the oracle, and the comparison rules."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+from rope_chunk_causal_amd import synth
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def say(*args) -> None:
+    """Name the case before a GPU step, flushed, so a crash log shows it."""
+    print("[gpu-case]", *args, file=sys.stderr, flush=True)
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    """numpy fp32 or bf16 bits -> contiguous GPU tensor of that dtype."""
+    t = torch()
+    if dtype == "bf16":
+        return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(t.bfloat16).cuda()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def to_host_f64(x) -> np.ndarray:
+    """GPU tensor (fp32/bf16) -> exact float64 numpy array."""
+    t = torch()
+    if x.dtype == t.bfloat16:
+        bits = x.detach().cpu().view(t.int16).numpy().view(np.uint16)
+        return synth.bf16_bits_to_f32(bits).astype(np.float64)
+    return x.detach().cpu().double().numpy()
+
+
+class Bf16Rows:
+    """Lazy float64 view of a bf16-bits array: widens only what is indexed."""
+
+    def __init__(self, bits: np.ndarray):
+        self.bits = bits
+        self.shape = bits.shape
+
+    def __getitem__(self, idx):
+        return synth.bf16_bits_to_f32(self.bits[idx]).astype(np.float64)
+
+
+def half_ulp_bf16(y: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |y| (8 significant bits)."""
+    a = np.maximum(np.abs(y), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 8)
+
+
+def check_bf16_rope(gpu: np.ndarray, ref: np.ndarray, label: str) -> dict:
+    """bf16 RoPE rule: |gpu - ref| <= max(1e-2, half_ulp_bf16(ref) + 1e-5) everywhere.
+
+    1e-2 holds wherever bf16 can represent the value that closely (|ref| < 4);
+    above that the bound is the correctly-rounded one.  Also returns the raw
+    max error and the count of elements beyond 1e-2 (all must have |ref| >= 4).
+    """
+    err = np.abs(gpu - ref)
+    bound = np.maximum(1e-2, half_ulp_bf16(ref) + 1e-5)
+    bad = err > bound
+    over = err > 1e-2
+    stats = {"label": label, "max_abs": float(err.max()) if err.size else 0.0,
+             "n_over_1e-2": int(over.sum()), "n": int(err.size)}
+    assert not bad.any(), (label, stats, float(err[bad].max()))
+    assert np.all(np.abs(ref[over]) >= 4.0 - 1e-6), (label, stats)
+    return stats
+
+
+def check_attn(gpu: np.ndarray, ref: np.ndarray, label: str,
+               max_abs: float = 2e-2, mean_abs: float = 2e-3, rel_l2: float = 1e-2) -> dict:
+    err = np.abs(gpu - ref)
+    rel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
+    stats = {"label": label, "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+             "rel_l2": rel}
+    assert np.isfinite(gpu).all(), (label, "non-finite output")
+    assert stats["max_abs"] <= max_abs and stats["mean_abs"] <= mean_abs and rel <= rel_l2, stats
+    return stats
+
+
+def scale_for(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

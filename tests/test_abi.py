@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every entry point include/rcc.h declares,
+and rejects bad arguments on the host (no GPU needed: these calls return
+before anything is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rope_chunk_causal_amd as rcc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rcc.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"RCC_API\s+[\w\s\*]+?\b(rcc_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared()) == set(rcc.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    if not os.path.exists(rcc.LIB_PATH):
+        pytest.skip("librcc.so not built")
+    lib = ctypes.CDLL(rcc.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert rcc.lib().rcc_status_string(rcc.RCC_ERR_RANGE) == b"RCC_ERR_RANGE"
+
+
+def test_tables_size_is_host_only():
+    cfg = rcc.rope_cfg(44, 42, 42, 1024, 64, 128)
+    assert rcc.rope3d_tables_floats(cfg) == 1024 * 44 + 64 * 42 + 128 * 42
+    with pytest.raises(rcc.RccError):
+        rcc.rope3d_tables_floats(rcc.rope_cfg(43, 42, 42, 1024, 64, 128))
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# Fake, aligned device addresses: every case below must fail a host check
+# first, so nothing is ever launched with them.  Skipped where a GPU exists.
+FAKE = 1 << 40
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dtype=7), rcc.RCC_ERR_DTYPE),
+    (dict(head_dim=24 + 4), rcc.RCC_ERR_SHAPE),
+    (dict(head_dim=136), rcc.RCC_ERR_SHAPE),
+    (dict(chunk_tokens=0), rcc.RCC_ERR_SHAPE),
+    (dict(q_pos=70), rcc.RCC_ERR_RANGE),
+    (dict(kv_tokens=97), rcc.RCC_ERR_RANGE),
+    (dict(q=0), rcc.RCC_ERR_NULL),
+    (dict(out=FAKE + 8), rcc.RCC_ERR_ALIGN),
+    (dict(q_tokens=-1), rcc.RCC_ERR_SHAPE),
+])
+def test_attn_host_checks(kw, status):
+    a = dict(in_dtype=rcc.RCC_F32, out_dtype=rcc.RCC_F32, batch=1, n_heads=2, head_dim=24,
+             q_tokens=32, q_pos=64, kv_tokens=96, chunk_tokens=32, scale=0.2, q=FAKE,
+             k=FAKE, v=FAKE, cache=96, out=FAKE)
+    a.update(kw)
+    st = rcc.lib().rcc_chunk_causal_attn(
+        a["in_dtype"], a["out_dtype"], a["batch"], a["n_heads"], a["head_dim"], a["q_tokens"],
+        a["q_pos"], a["kv_tokens"], a["chunk_tokens"], a["scale"], a["q"], a["k"], a["v"],
+        a["cache"], a["out"], None)
+    assert st == status, rcc.lib().rcc_last_error()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+@pytest.mark.parametrize("kw,status", [
+    (dict(cfg=rcc.rope_cfg(8, 8, 7, 16, 4, 4)), rcc.RCC_ERR_SHAPE),     # odd band
+    (dict(cfg=rcc.rope_cfg(8, 8, 4, 16, 4, 4)), rcc.RCC_ERR_SHAPE),     # D = 20, not 8k
+    (dict(grid=rcc.grid(2, 4, 4, 15, 0)), rcc.RCC_ERR_RANGE),            # s + F > max_t
+    (dict(grid=rcc.grid(2, 5, 4, 0, 0)), rcc.RCC_ERR_RANGE),             # H > max_h
+    (dict(grid=rcc.grid(2, 4, 4, 0, 1)), rcc.RCC_ERR_RANGE),             # Delta + n > FHW
+    (dict(grid=rcc.grid(2, 4, 4, -1, 0)), rcc.RCC_ERR_RANGE),            # s < 0
+    (dict(grid=rcc.grid(0, 4, 4, 0, 0)), rcc.RCC_ERR_SHAPE),             # empty grid
+    (dict(cache=95), rcc.RCC_ERR_RANGE),                                 # cache too small
+    (dict(in_dtype=3), rcc.RCC_ERR_DTYPE),
+    (dict(batch=0), rcc.RCC_ERR_SHAPE),
+    (dict(v=0), rcc.RCC_ERR_NULL),
+    (dict(k=FAKE + 4), rcc.RCC_ERR_ALIGN),
+    (dict(q_out=FAKE, out_dtype=rcc.RCC_BF16), rcc.RCC_ERR_DTYPE),     # in-place, mixed dtype
+])
+def test_apply_host_checks(kw, status):
+    a = dict(cfg=rcc.rope_cfg(8, 8, 8, 16, 4, 4), grid=rcc.grid(2, 4, 4, 4, 0),
+             in_dtype=rcc.RCC_F32, out_dtype=rcc.RCC_F32, batch=1, n=32, nh=2,
+             q=FAKE, k=FAKE, v=FAKE, q_out=FAKE + 4096, kc=FAKE, vc=FAKE, cache=96)
+    a.update(kw)
+    st = rcc.lib().rcc_rope3d_apply_append(
+        ctypes.byref(a["cfg"]), FAKE, ctypes.byref(a["grid"]), a["in_dtype"], a["out_dtype"],
+        a["batch"], a["n"], a["nh"], a["q"], a["k"], a["v"], a["q_out"], a["kc"], a["vc"],
+        a["cache"], None)
+    assert st == status, rcc.lib().rcc_last_error()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+def test_positions_and_tables_host_checks():
+    L = rcc.lib()
+    g = rcc.grid(2, 4, 4, 0, 30)
+    assert L.rcc_rope3d_positions(ctypes.byref(g), 3, FAKE, None) == rcc.RCC_ERR_RANGE
+    assert L.rcc_rope3d_positions(ctypes.byref(g), 2, 0, None) == rcc.RCC_ERR_NULL
+    assert L.rcc_rope3d_positions(ctypes.byref(g), 0, 0, None) == rcc.RCC_OK
+    bad = rcc.rope_cfg(8, 8, 8, 16, 4, 0)
+    assert L.rcc_rope3d_tables(ctypes.byref(bad), FAKE, None) == rcc.RCC_ERR_SHAPE
+    good = rcc.rope_cfg(8, 8, 8, 16, 4, 4)
+    assert L.rcc_rope3d_tables(ctypes.byref(good), FAKE + 4, None) == rcc.RCC_ERR_ALIGN
