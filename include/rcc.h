@@ -149,11 +149,12 @@ RCC_API rcc_status rcc_rope3d_apply_append(
  *   out      [batch, q_tokens, n_heads, head_dim] in `out_dtype`.
  * Key j is visible to query i iff j < kv_tokens and
  * floor(j / chunk_tokens) <= floor((q_pos + i) / chunk_tokens).
- * out = softmax(scale * q k^T over visible keys) v.  Operands are rounded
+ * out = softmax(scale * q k^T over visible keys) v, scale > 0.  Operands are rounded
  * to bf16 (nearest-even) for the matrix cores; accumulation and softmax
  * state are fp32.
  * Errors: NULL; DTYPE; SHAPE (head_dim not a multiple of 8 in [8, 128],
- * batch/n_heads/chunk_tokens non-positive, q_tokens < 0); RANGE
+ * batch/n_heads/chunk_tokens non-positive, q_tokens < 0, scale not positive
+ * and finite); RANGE
  * (q_pos < 0, q_pos + q_tokens > kv_tokens, kv_tokens > cache_tokens,
  * sizes >= 2^31); ALIGN; HIP.
  */

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librcc.so")
-SOURCES = ["rcc_abi.cpp", "rope3d.hip", "attn.hip"]
+SOURCES = ["rcc_abi.cpp", "rope3d.hip", "attn.hip", "attn_d128.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.

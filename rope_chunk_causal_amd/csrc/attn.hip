@@ -251,6 +251,7 @@ hipError_t launch_dp(const AttnArgs& a, rcc_dtype in, rcc_dtype out, hipStream_t
 hipError_t launch_chunk_causal_attn(const AttnArgs& a, rcc_dtype in, rcc_dtype out,
                                     hipStream_t s) {
   if (a.q_tokens == 0) return hipSuccess;
+  if (attn_d128_supported(a, in)) return launch_attn_d128(a, out, s);
   if (a.head_dim <= 32) return launch_dp<32>(a, in, out, s);
   if (a.head_dim <= 64) return launch_dp<64>(a, in, out, s);
   return launch_dp<128>(a, in, out, s);

@@ -188,7 +188,8 @@ rcc_status rcc_chunk_causal_attn(
   if (n_heads <= 0 || n_heads > 65535) return fail(RCC_ERR_SHAPE, "n_heads must be in [1, 65535]");
   if (chunk_tokens <= 0) return fail(RCC_ERR_SHAPE, "chunk_tokens must be positive");
   if (q_tokens < 0) return fail(RCC_ERR_SHAPE, "q_tokens < 0");
-  if (!isfinite(scale)) return fail(RCC_ERR_SHAPE, "scale must be finite");
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(RCC_ERR_SHAPE, "scale must be positive and finite");
   if (q_pos < 0 || q_pos + q_tokens > kv_tokens)
     return fail(RCC_ERR_RANGE, "query rows [%lld, %lld) not inside the %lld visible keys",
                 (long long)q_pos, (long long)(q_pos + q_tokens), (long long)kv_tokens);

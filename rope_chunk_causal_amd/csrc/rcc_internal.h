@@ -73,5 +73,8 @@ struct AttnArgs {
 };
 hipError_t launch_chunk_causal_attn(const AttnArgs& a, rcc_dtype in, rcc_dtype out,
                                     hipStream_t s);
+// bf16, head_dim 128 fast path (attn_d128.hip).
+bool attn_d128_supported(const AttnArgs& a, rcc_dtype in);
+hipError_t launch_attn_d128(const AttnArgs& a, rcc_dtype out, hipStream_t s);
 
 }  // namespace rcc

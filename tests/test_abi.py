@@ -62,6 +62,8 @@ FAKE = 1 << 40
     (dict(q=0), rcc.RCC_ERR_NULL),
     (dict(out=FAKE + 8), rcc.RCC_ERR_ALIGN),
     (dict(q_tokens=-1), rcc.RCC_ERR_SHAPE),
+    (dict(scale=0.0), rcc.RCC_ERR_SHAPE),
+    (dict(scale=-0.1), rcc.RCC_ERR_SHAPE),
 ])
 def test_attn_host_checks(kw, status):
     a = dict(in_dtype=rcc.RCC_F32, out_dtype=rcc.RCC_F32, batch=1, n_heads=2, head_dim=24,
