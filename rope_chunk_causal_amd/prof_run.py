@@ -1,0 +1,91 @@
+"""Run one workload of the hot path a few times, for rocprofv3 collection.
+
+    python -m rope_chunk_causal_amd.prof_run WORKLOAD [--reps N]
+
+WORKLOAD: attn_480p (chunk_causal_attn, 4680 queries over 14040 keys, 12
+heads), attn_720p (10800 over 75600, 40 heads), rope_480p (one 4680-token
+chunk, 12 heads), rope_sp_b64 (585-token rank slice, 64 chunks batched),
+copy (a plain 1 GiB device-to-device copy: the reference for scaling HBM
+byte counters), all (every one of them, in that order).  Inputs are seeded
+N(0,1) bf16 on the device; nothing is checked here (the tests do that).
+"""
+from __future__ import annotations
+
+import argparse
+import math
+
+import torch
+
+import rope_chunk_causal_amd as rcc
+from rope_chunk_causal_amd import synth
+
+COPY_BYTES = 1 << 30
+
+
+def _randn(gen, *shape):
+    return torch.randn(*shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def attn(name: str, reps: int, gen) -> None:
+    wl = synth.WORKLOADS["480p_step" if name == "attn_480p" else "720p_step"]
+    s = wl.start_frames[0]
+    kv = (s + wl.frames) * wl.hw
+    q = _randn(gen, 1, wl.chunk_tokens, wl.n_heads, wl.head_dim)
+    k = _randn(gen, 1, kv, wl.n_heads, wl.head_dim)
+    v = _randn(gen, 1, kv, wl.n_heads, wl.head_dim)
+    o = torch.empty_like(q)
+    for _ in range(reps):
+        rcc.chunk_causal_attn(q, k, v, o, s * wl.hw, kv, wl.chunk_tokens, 1 / math.sqrt(wl.head_dim))
+
+
+def rope(name: str, reps: int, gen) -> None:
+    wl = synth.WORKLOADS["480p_step" if name == "rope_480p" else "480p_sp_shard"]
+    s = wl.start_frames[0]
+    if name == "rope_480p":
+        batch, n, off = 1, wl.chunk_tokens, 0
+    else:
+        batch, n, off = 64, wl.chunk_tokens // synth.SP_DEGREE, 2 * (wl.chunk_tokens // synth.SP_DEGREE)
+    r = wl.rope
+    cfg = rcc.rope_cfg(r.d_t, r.d_h, r.d_w, r.max_t, r.max_h, r.max_w, r.theta)
+    tables = rcc.rope3d_tables(cfg)
+    cap = (s + wl.frames) * wl.hw
+    q, k, v = (_randn(gen, batch, n, wl.n_heads, wl.head_dim) for _ in range(3))
+    qo = torch.empty_like(q)
+    kc = torch.empty(batch, cap, wl.n_heads, wl.head_dim, device="cuda", dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+    g = rcc.grid(wl.frames, wl.height, wl.width, s, off)
+    for _ in range(reps):
+        rcc.rope3d_apply_append(cfg, tables, g, q, k, v, qo, kc, vc)
+
+
+def copy(reps: int) -> None:
+    a = torch.ones(COPY_BYTES // 2, device="cuda", dtype=torch.bfloat16)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+
+
+def main() -> None:
+    p = argparse.ArgumentParser()
+    p.add_argument("workload", choices=["attn_480p", "attn_720p", "rope_480p", "rope_sp_b64",
+                                        "copy", "all"])
+    p.add_argument("--reps", type=int, default=3)
+    a = p.parse_args()
+    rcc.lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    names = ["copy", "attn_480p", "attn_720p", "rope_480p", "rope_sp_b64"] \
+        if a.workload == "all" else [a.workload]
+    for n in names:
+        if n == "copy":
+            copy(a.reps)
+        elif n.startswith("attn"):
+            attn(n, a.reps, gen)
+        else:
+            rope(n, a.reps, gen)
+        torch.cuda.synchronize()
+        print(f"{n}: {a.reps} reps done", flush=True)
+
+
+if __name__ == "__main__":
+    main()
