@@ -7,9 +7,14 @@
 // and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, P^T kept in registers).
 //
 // What this kernel adds for the bf16 / head_dim-128 shape:
-// * K and V tiles move global -> LDS with global_load_lds_dwordx4 (no VGPR
-//   staging), double-buffered: the loads of tile j+1 are in flight while
-//   tile j is computed, with one workgroup barrier per tile.
+// * One workgroup of 8 waves (256 query rows, two waves per SIMD) per CU, so
+//   each K/V tile moves from L2 into LDS once per 256 rows.
+// * K and V move global -> LDS with global_load_lds_dwordx4 (no VGPR
+//   staging) in 32-key tiles through a ring of four LDS stages: tile t is
+//   computed while tiles t+1 and t+2 are in flight and tile t+3 starts into
+//   the stage tile t-1 used.  One workgroup barrier per tile; the wait before
+//   it counts only the loads of tile t.  (A two-stage ring that waits for the
+//   next tile each step leaves the MFMAs idle for much of the L2 latency.)
 // * Both tiles stay row-major (256 B per key) with an XOR swizzle of the
 //   16-byte chunk index chosen per use, so every LDS read is bank-conflict
 //   free: K chunk c of key r sits at c ^ (r % 16) (ds_read_b128 of 16 keys at
@@ -29,13 +34,14 @@ namespace rcc {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;      // query rows per workgroup
-constexpr int kBN = 64;               // keys per tile
+constexpr int kBN = 32;               // keys per tile
 constexpr int kRowBytes = kD * 2;     // 256 B per key row
-constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
+constexpr int kTileBytes = kBN * kRowBytes;  // 8 KB
 constexpr int kXcds = 8;
+constexpr int kStages = 4;            // K/V tiles resident in LDS
 constexpr float kLazy = 8.0f;         // log2 headroom before a rescale
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -54,58 +60,51 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// DMA layout of a tile: instruction i (0..3) of wave w moves 1 KB = key rows
-// 16 i + 4 w + (0..3) into LDS bytes [(4 i + w) KB, +1 KB); lane -> (row
-// 16 i + 4 w + lane/16, LDS chunk slot lane%16).  With this assignment the
-// swizzle of every lane is the same for all four instructions, so a lane
-// needs one K and one V byte offset; instruction i adds 16 rows.
+// DMA layout of a tile: wave w moves 1 KB = key rows 4 w + (0..3) into LDS
+// bytes [w KB, +1 KB); lane -> (row 4 w + lane/16, LDS chunk slot lane%16).
 struct Dma {
-  uint32_t k, v;      // lane's byte offset inside the tile for instruction 0
-  uint32_t step;      // bytes of 16 key rows
+  uint32_t k, v;      // lane's byte offset inside its key row (swizzled chunk)
 };
 
 __device__ __forceinline__ Dma dma_offsets(int64_t rs, int wave, int lane) {
   const int sub = lane >> 4;
   const int cpos = lane & 15;
-  const int r = 4 * wave + sub;       // row of instruction 0; r % 16 == r, r % 4 == sub
+  const int r = 4 * wave + sub;       // 0..31
   Dma d;
-  d.k = (uint32_t)(r * rs * 2 + ((cpos ^ r) << 4));
-  d.v = (uint32_t)(r * rs * 2 + ((cpos ^ (sub << 2)) << 4));
-  d.step = (uint32_t)(16 * rs * 2);
+  d.k = (uint32_t)((cpos ^ (r & 15)) << 4);
+  d.v = (uint32_t)((cpos ^ (sub << 2)) << 4);
   return d;
 }
 
-// Issue this wave's share of one K tile and one V tile (keys j0 .. j0+63).
-// Full tiles use a uniform base pointer plus the per-lane offsets; a ragged
-// last tile clamps rows past kv_end to the last key (their scores are masked
-// and their P is 0).
+// Issue this wave's share of one K and one V tile (keys j0 .. j0+31).  Key
+// indices are clamped to kv_end - 1: a ragged last tile re-reads the last key
+// for rows past kv_end (their scores are masked), and a tile past the end (the
+// pipeline always runs three tiles ahead) re-reads it into a stage no step
+// reads again.  Branch-free, so the compiler tracks which stage each load
+// writes.  Offsets are 32-bit from the (batch, head) base: the host limits a
+// batch's cache to 4 GiB.
 __device__ __forceinline__ void issue_tile(const __bf16* kg, const __bf16* vg, int64_t rs,
                                            int j0, int kv_end, const Dma& d, char* ks,
                                            char* vs, int wave, int lane) {
-  if (j0 + kBN <= kv_end) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* kb = reinterpret_cast<const char*>(kg + (int64_t)j0 * rs) + i * d.step;
-      const char* vb = reinterpret_cast<const char*>(vg + (int64_t)j0 * rs) + i * d.step;
-      __builtin_amdgcn_global_load_lds(kb + d.k, (lds_void*)(ks + (4 * i + wave) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + d.v, (lds_void*)(vs + (4 * i + wave) * 1024), 16, 0, 0);
-    }
-    return;
-  }
-  const int sub = lane >> 4;
-  const int cpos = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * i + 4 * wave + sub;
-    int key = j0 + r;
-    key = key < kv_end ? key : kv_end - 1;
-    const int ck = cpos ^ (r & 15);
-    const int cv = cpos ^ ((r & 3) << 2);
-    __builtin_amdgcn_global_load_lds(kg + (int64_t)key * rs + ck * 8,
-                                     (lds_void*)(ks + (4 * i + wave) * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vg + (int64_t)key * rs + cv * 8,
-                                     (lds_void*)(vs + (4 * i + wave) * 1024), 16, 0, 0);
-  }
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const int key = min(j0 + 4 * wave + (lane >> 4), kv_end - 1);
+  const uint32_t row = (uint32_t)key * row_bytes;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kg) + (row + d.k),
+                                   (lds_void*)(ks + wave * 1024), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vg) + (row + d.v),
+                                   (lds_void*)(vs + wave * 1024), 16, 0, 0);
+}
+
+// Wait until at most n of this wave's DMA instructions are in flight (n is
+// 2 per tile: 1 K + 1 V), then a workgroup barrier.  The barrier carries no
+// memory fence: a fence would also wait for the later tiles' loads.
+template <int n>
+__device__ __forceinline__ void tile_ready() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Per-wave state carried across key tiles.
@@ -116,50 +115,34 @@ struct WaveState {
 
 // Per-lane constants of one workgroup.
 struct Lane {
-  int koff[2][8];   // K-fragment byte offsets in a tile
+  int koff[8];      // K-fragment byte offsets in a tile
   int voff[4];      // V^T-fragment byte offsets in a tile (+ kq*16 rows, +8 rows)
   int g, lim;
 };
 
-// One key tile read from stage buffers (ks, vs); the tile after it is already
-// being loaded into the other stage.  ks/vs are distinct __shared__ objects
-// per stage, so the compiler does not order these LDS reads after the other
-// stage's DMA writes.
+// One 32-key tile read from stage buffers (ks, vs); later tiles are already
+// being loaded into other stages.  Each stage is a distinct __shared__ object,
+// so the compiler does not order these LDS reads after the other stages' DMA
+// writes.
 __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf16x8 (&qf)[8],
                                           const char* ks, const char* vs, int j0, int lim_lo,
                                           float c2) {
-  // S^T = K Q^T: the two 32-key blocks interleaved; the schedule below keeps
-  // the fragment reads two k-steps ahead of the MFMAs that consume them.
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
-  bf16x8 ka[8], kb[8];
+  // S^T = K Q^T, fragment reads kept ahead of the MFMAs that consume them.
+  f32x16 s0 = f32x16{};
+  bf16x8 ka[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    ka[kk] = *reinterpret_cast<const bf16x8*>(ks + L.koff[0][kk]);
-    kb[kk] = *reinterpret_cast<const bf16x8*>(ks + L.koff[1][kk]);
-  }
+  for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const bf16x8*>(ks + L.koff[kk]);
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    s0 = mfma32(ka[kk], qf[kk], s0);
-    s1 = mfma32(kb[kk], qf[kk], s1);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads, k-steps 0-1
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // DS reads, k-step i+2
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // MFMAs, k-step i
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMAs, k-steps 6-7
+  for (int kk = 0; kk < 8; ++kk) s0 = mfma32(ka[kk], qf[kk], s0);
 
   if (j0 + kBN > lim_lo) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + (r >> 2) * 8 + L.g * 4 + (r & 3);
       s0[r] = key < L.lim ? s0[r] : -INFINITY;
-      s1[r] = key + 32 < L.lim ? s1[r] : -INFINITY;
     }
   }
 
-  // V^T fragments of the first 16-key block, read before the softmax math.
   auto vread = [&](int kq, int dt) {
     const int base = kq * 16 * kRowBytes + L.voff[dt];
     // Whole-vector form: building the operand element by element from the
@@ -169,13 +152,16 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
         __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vs + base + 8 * kRowBytes));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  bf16x8 vcur[4];
+  bf16x8 vf[2][4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) vcur[dt] = vread(0, dt);
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vf[kq][dt] = vread(kq, dt);
 
-  float mx = fmaxf(s0[0], s1[0]);
+  float mx = s0[0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);  // v_max3_f32
+  for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);  // v_max3_f32
+  mx = fmaxf(mx, s0[15]);
   mx = xhalf_max(mx) * c2;
   // Lazy rescale: move the reference max only when it would grow by > 2^8.
   const float m_use = (mx - w.m_run > kLazy) ? mx : w.m_run;
@@ -190,43 +176,37 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
   }
 
   float rsum = 0.f;
-  bf16x8 pf[4];
+  bf16x8 pf[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -w.m_run));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -w.m_run));
-    rsum += p0 + p1;
-    pf[r >> 3][r & 7] = (__bf16)p0;
-    pf[2 + (r >> 3)][r & 7] = (__bf16)p1;
+    const float p = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -w.m_run));
+    rsum += p;
+    pf[r >> 3][r & 7] = (__bf16)p;
   }
   w.l_run += xhalf_sum(rsum);
 
-  // O^T += V^T P^T, next block's V^T fragments read one block ahead.
 #pragma unroll
-  for (int kq = 0; kq < 4; ++kq) {
-    bf16x8 vnext[4];
-    if (kq + 1 < 4) {
+  for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vnext[dt] = vread(kq + 1, dt);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) w.oacc[dt] = mfma32(vcur[dt], pf[kq], w.oacc[dt]);
-    if (kq + 1 < 4) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vcur[dt] = vnext[dt];
-    }
-  }
+    for (int dt = 0; dt < 4; ++dt) w.oacc[dt] = mfma32(vf[kq][dt], pf[kq], w.oacc[dt]);
 }
 
 template <typename Tout>
-__global__ __launch_bounds__(kThreads, 2) void attn_d128_kernel(AttnArgs a, int n_qt) {
-  __shared__ __align__(1024) char sK0[kTileBytes];
-  __shared__ __align__(1024) char sV0[kTileBytes];
-  __shared__ __align__(1024) char sK1[kTileBytes];
-  __shared__ __align__(1024) char sV1[kTileBytes];
+__global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int n_qt) {
+  // One object per stage: K tile at +0, V tile at +8 KB.  All stages lie
+  // below 64 KB, so every fragment read addresses its stage with the 16-bit
+  // immediate offset of ds_read.
+  __shared__ __align__(1024) char sS0[2 * kTileBytes];
+  __shared__ __align__(1024) char sS1[2 * kTileBytes];
+  __shared__ __align__(1024) char sS2[2 * kTileBytes];
+  __shared__ __align__(1024) char sS3[2 * kTileBytes];
+  char* const sK0 = sS0; char* const sV0 = sS0 + kTileBytes;
+  char* const sK1 = sS1; char* const sV1 = sS1 + kTileBytes;
+  char* const sK2 = sS2; char* const sV2 = sS2 + kTileBytes;
+  char* const sK3 = sS3; char* const sV3 = sS3 + kTileBytes;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -257,24 +237,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d128_kernel(AttnArgs a, int 
   const int kv_end = min(a.kv_tokens, ((a.q_pos + qlast) / C + 1) * C);
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
-  const Dma dma = dma_offsets(rs, wave, lane);
-  issue_tile(kg, vg, rs, 0, kv_end, dma, sK0, sV0, wave, lane);
-
-  // Q^T operand fragments (rows past q_tokens read the last row; never stored).
+  // Q^T operand fragments (rows past q_tokens read the last row; never stored),
+  // loaded before the first K/V tiles so the per-tile waits below count only
+  // tile loads.
   bf16x8 qf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qclamp * rs + kk * 16 + g * 8);
 
+  const Dma dma = dma_offsets(rs, wave, lane);
+  issue_tile(kg, vg, rs, 0, kv_end, dma, sK0, sV0, wave, lane);
+  issue_tile(kg, vg, rs, kBN, kv_end, dma, sK1, sV1, wave, lane);
+  issue_tile(kg, vg, rs, 2 * kBN, kv_end, dma, sK2, sV2, wave, lane);
+
   Lane L;
   L.g = g;
   L.lim = min(a.kv_tokens, ((a.q_pos + qclamp) / C + 1) * C);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int r = kb * 32 + l32;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) L.koff[kb][kk] = r * kRowBytes + (((kk * 2 + g) ^ (r & 15)) << 4);
-  }
+  for (int kk = 0; kk < 8; ++kk) L.koff[kk] = l32 * kRowBytes + (((kk * 2 + g) ^ (l32 & 15)) << 4);
   {
     const int G = lane >> 4, j = lane & 15;
     const int vrow = (G >> 1) * 4 + (j >> 2);
@@ -293,18 +273,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d128_kernel(AttnArgs a, int 
   w.l_run = 0.f;
   const float c2 = a.scale_log2;
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(kg, vg, rs, (t + 1) * kBN, kv_end, dma, sK1, sV1, wave, lane);
-    tile_step(w, L, qf, sK0, sV0, t * kBN, lim_lo, c2);
-    if (t + 1 < n_tiles) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t + 2 < n_tiles) issue_tile(kg, vg, rs, (t + 2) * kBN, kv_end, dma, sK0, sV0, wave, lane);
-      tile_step(w, L, qf, sK1, sV1, (t + 1) * kBN, lim_lo, c2);
-    }
+  // Tile t lives in stage t % 4; tiles t+1 and t+2 are in flight while it is
+  // computed, and tile t+3 starts into the stage that tile t-1 used.
+  auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn) {
+    tile_ready<4>();
+    issue_tile(kg, vg, rs, (t + 3) * kBN, kv_end, dma, kn, vn, wave, lane);
+    tile_step(w, L, qf, ks, vs, t * kBN, lim_lo, c2);
+  };
+  int t = 0;
+  for (; t + kStages <= n_tiles; t += kStages) {
+    step(t, sK0, sV0, sK3, sV3);
+    step(t + 1, sK1, sV1, sK0, sV0);
+    step(t + 2, sK2, sV2, sK1, sV1);
+    step(t + 3, sK3, sV3, sK2, sV2);
   }
+  if (t < n_tiles) step(t, sK0, sV0, sK3, sV3);
+  if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0);
+  if (t + 2 < n_tiles) step(t + 2, sK2, sV2, sK1, sV1);
+  // No load may still be writing this workgroup's LDS when it exits.
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (qrow < a.q_tokens) {
     const float inv = 1.f / w.l_run;
@@ -330,7 +317,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d128_kernel(AttnArgs a, int 
 }  // namespace
 
 bool attn_d128_supported(const AttnArgs& a, rcc_dtype in) {
-  return in == RCC_BF16 && a.head_dim == kD;
+  // K/V loads use 32-bit byte offsets inside one batch entry's cache.
+  const int64_t cache_bytes = (int64_t)a.cache_tokens * a.n_heads * kRowBytes;
+  return in == RCC_BF16 && a.head_dim == kD && cache_bytes <= (int64_t)UINT32_MAX;
 }
 
 hipError_t launch_attn_d128(const AttnArgs& a, rcc_dtype out, hipStream_t s) {
