@@ -20,9 +20,12 @@ section by section:
 * ``attention`` — attention of a query chunk over the cache (Algorithm 3
                   step 6) with the block-causal visibility rule (§3.2,
                   §3.3 block-wise autoregression).
+* ``qkv``       — the local QKV projection (Algorithm 3 step 1) followed by
+                  Causal-RoPE and the cache write: the fusion of §3.4.1
+                  item 3.
 
 Every function here is pinned by the ``-m "not gpu"`` tests against facts
 fixed by the pages or by mathematics (closed forms, invariants, brute force
 on tiny inputs, library special cases); none is "parity unpinned".
 """
-from . import rope3d, attention  # noqa: F401
+from . import rope3d, attention, qkv  # noqa: F401

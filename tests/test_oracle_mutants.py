@@ -9,8 +9,10 @@ import numpy as np
 import pytest
 
 import test_oracle_attention as TA
+import test_oracle_qkv as TQ
 import test_oracle_rope as TR
 from oracle import attention as A
+from oracle import qkv as Q
 from oracle import rope3d as R
 
 _orig_token_freqs = R.token_freqs
@@ -80,6 +82,30 @@ def _mut_attn_no_scale(q, kc, vc, q_pos, kv_len, C, scale, rows=None, block=256)
     return _orig_attn(q, kc, vc, q_pos, kv_len, C, 1.0, rows=rows, block=block)
 
 
+_orig_project = Q.qkv_project
+
+
+def _mut_qkv_k_v_swapped(x, w, bias, nh, d):
+    q, k, v = _orig_project(x, w, bias, nh, d)
+    return q, v, k
+
+
+def _mut_qkv_d_major(x, w, bias, nh, d):
+    """Rows of each group read as head_dim-major instead of head-major."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x @ np.asarray(w, dtype=np.float64).T
+    if bias is not None:
+        y = y + bias
+    b, n = x.shape[:2]
+    hd = nh * d
+    return tuple(y[..., i * hd:(i + 1) * hd].reshape(b, n, d, nh).transpose(0, 1, 3, 2)
+                 for i in range(3))
+
+
+def _mut_qkv_no_bias(x, w, bias, nh, d):
+    return _orig_project(x, w, None, nh, d)
+
+
 ROPE_PINS = [
     (TR.test_rotation_matches_gptj_interleaved_rope_per_band, ((8, 8, 8),)),
     (TR.test_unit_vector_closed_form, ()),
@@ -87,6 +113,12 @@ ROPE_PINS = [
     (TR.test_positions_brute_force_grid, (3, 5, 7, 9)),
     (TR.test_start_frame_worked_example, ()),
     (TR.test_shard_equals_unsharded_algorithm2, (8,)),
+]
+
+QKV_PINS = [
+    (TQ.test_projection_brute_force, ()),
+    (TQ.test_identity_projection, ()),
+    (TQ.test_one_hot_row_lands_in_its_slot, (1, 2, 7)),
 ]
 
 ATTN_PINS = [
@@ -118,6 +150,12 @@ def test_attention_mutant_is_caught(monkeypatch, attr, mutant):
     assert any(_fails(fn, *args) for fn, args in ATTN_PINS), f"{mutant.__name__} survived"
 
 
+@pytest.mark.parametrize("mutant", [_mut_qkv_k_v_swapped, _mut_qkv_d_major, _mut_qkv_no_bias])
+def test_qkv_mutant_is_caught(monkeypatch, mutant):
+    monkeypatch.setattr(Q, "qkv_project", mutant)
+    assert any(_fails(fn, *args) for fn, args in QKV_PINS), f"{mutant.__name__} survived"
+
+
 def test_unmutated_oracle_passes_every_pin():
-    for fn, args in ROPE_PINS + ATTN_PINS:
+    for fn, args in ROPE_PINS + ATTN_PINS + QKV_PINS:
         assert not _fails(fn, *args), fn.__name__
