@@ -166,6 +166,34 @@ RCC_API rcc_status rcc_chunk_causal_attn(
     const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
     void* out, hipStream_t stream);
 
+/*
+ * qkv_rope_append — the local QKV projection fused with Causal-RoPE and the
+ * KV-cache write ([YL] §3.4.1 item 3: QKV projection and Causal-RoPE in one
+ * kernel; Algorithm 3 steps 1-3 and 5).  All tensors bf16 except the bias.
+ *   x        [batch, n_tokens, model_dim]: the call's token slice.
+ *   w_qkv    [3 * n_heads * D, model_dim], D = d_t + d_h + d_w: the rows of
+ *            the q, k and v projections stacked in that order, each group
+ *            head-major then head_dim (a fused Linear's weight).
+ *   bias     fp32 [3 * n_heads * D], or NULL for none.
+ *   q_out    [batch, n_tokens, n_heads, D].
+ *   k_cache, v_cache [batch, cache_tokens, n_heads, D].
+ * y = x w_qkv^T + bias is accumulated in fp32 from bf16 operands; its q and
+ * k parts are rotated in fp32 exactly as rope3d_apply_append rotates them
+ * (tables, grid, rows s*H*W + Delta + [0, n_tokens)) and rounded to bf16
+ * (nearest-even) once, at the store.  q_out gets rotated q; the cache rows
+ * of the slice get rotated k and the unrotated v; nothing else is written.
+ * Errors: NULL (bias may be NULL); SHAPE (D != d_t + d_h + d_w, D % 32 != 0,
+ * model_dim not a positive multiple of 16, batch, n_heads or grid
+ * non-positive, n_tokens < 0, x or w_qkv of 4 GiB or more); RANGE (as
+ * rope3d_apply_append); ALIGN (16 bytes; bias 4 bytes); HIP.
+ */
+RCC_API rcc_status rcc_qkv_rope_append(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    int32_t batch, int64_t n_tokens, int32_t n_heads, int32_t model_dim,
+    const void* x, const void* w_qkv, const float* bias,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream);
+
 /* Static string naming a status code. */
 RCC_API const char* rcc_status_string(rcc_status s);
 

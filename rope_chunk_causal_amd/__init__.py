@@ -22,8 +22,8 @@ RCC_OK, RCC_ERR_NULL, RCC_ERR_SHAPE, RCC_ERR_RANGE, RCC_ERR_DTYPE, RCC_ERR_ALIGN
 RCC_F32, RCC_BF16 = 0, 1
 
 EXPORTS = ("rcc_rope3d_tables_floats", "rcc_rope3d_tables", "rcc_rope3d_positions",
-           "rcc_rope3d_apply_append", "rcc_chunk_causal_attn", "rcc_status_string",
-           "rcc_last_error")
+           "rcc_rope3d_apply_append", "rcc_qkv_rope_append", "rcc_chunk_causal_attn",
+           "rcc_status_string", "rcc_last_error")
 
 
 class RccError(RuntimeError):
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.rcc_rope3d_apply_append.argtypes = [cfgp, P, gridp, ctypes.c_int, ctypes.c_int,
                                           I32, I64, I32, P, P, P, P, P, P, I64, P]
     L.rcc_rope3d_apply_append.restype = ctypes.c_int
+    L.rcc_qkv_rope_append.argtypes = [cfgp, P, gridp, I32, I64, I32, I32, P, P, P, P, P, P, I64, P]
+    L.rcc_qkv_rope_append.restype = ctypes.c_int
     L.rcc_chunk_causal_attn.argtypes = [ctypes.c_int, ctypes.c_int, I32, I32, I32,
                                         I64, I64, I64, I64, F, P, P, P, I64, P, P]
     L.rcc_chunk_causal_attn.restype = ctypes.c_int
@@ -190,6 +192,37 @@ def rope3d_apply_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, q, k, v, q_out
         _ptr(q_out, "q_out", numel), _ptr(k_cache, "k_cache", B * cap * nh * D),
         _ptr(v_cache, "v_cache", B * cap * nh * D), cap, _stream(stream)),
         "rope3d_apply_append")
+
+
+def qkv_rope_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, x, w_qkv, bias, q_out,
+                    k_cache, v_cache, stream=None) -> None:
+    """x [B, n, model_dim] bf16; w_qkv [3*heads*D, model_dim] bf16; bias fp32
+    [3*heads*D] or None; q_out [B, n, heads, D] bf16; caches [B, cache_tokens,
+    heads, D] bf16."""
+    torch = _torch()
+    if x.dim() != 3 or q_out.dim() != 4 or tuple(q_out.shape[:2]) != tuple(x.shape[:2]):
+        raise ValueError("x must be [B, n, model_dim] and q_out [B, n, heads, D]")
+    B, n, K = x.shape
+    nh, D = q_out.shape[2], q_out.shape[3]
+    if tuple(w_qkv.shape) != (3 * nh * D, K):
+        raise ValueError("w_qkv must be [3 * heads * D, model_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or \
+            k_cache.shape[0] != B or tuple(k_cache.shape[2:]) != (nh, D):
+        raise ValueError("caches must be [B, cache_tokens, heads, D]")
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("q_out", q_out), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != 3 * nh * D):
+        raise TypeError("bias must be float32 [3 * heads * D] or None")
+    cap = k_cache.shape[1]
+    ntab = rope3d_tables_floats(cfg)
+    _check(lib().rcc_qkv_rope_append(
+        ctypes.byref(cfg), _ptr(tables, "tables", ntab, torch.float32), ctypes.byref(g),
+        B, n, nh, K, _ptr(x, "x", B * n * K), _ptr(w_qkv, "w_qkv", 3 * nh * D * K),
+        _ptr(bias, "bias", 3 * nh * D), _ptr(q_out, "q_out", B * n * nh * D),
+        _ptr(k_cache, "k_cache", B * cap * nh * D), _ptr(v_cache, "v_cache", B * cap * nh * D),
+        cap, _stream(stream)), "qkv_rope_append")
 
 
 def chunk_causal_attn(q, k_cache, v_cache, out, q_pos: int, kv_tokens: int,

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librcc.so")
-SOURCES = ["rcc_abi.cpp", "rope3d.hip", "attn.hip", "attn_d128.hip"]
+SOURCES = ["rcc_abi.cpp", "rope3d.hip", "attn.hip", "attn_d128.hip", "qkv_rope.hip"]
 # The fast attention kernel never relies on NaN semantics (masking uses
 # -inf); without NaN honouring fmaxf needs no quieting of its operands.
 FILE_FLAGS = {"attn_d128.hip": ["-fno-honor-nans"]}

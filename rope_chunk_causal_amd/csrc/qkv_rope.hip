@@ -1,0 +1,235 @@
+// Fused QKV projection + Causal-RoPE + KV-cache write, bf16.
+//
+// [YL] Yuan & Li, "Accelerating Video Generation Inference with
+// Sequential-Parallel 3D Positional Encoding Using a Global Time Index",
+// §3.4.1 item 3 (QKV projection and Causal-RoPE fused into one kernel) and
+// Algorithm 3 steps 1-3 and 5: y = x W^T (+ b) for the rank's token slice,
+// q and k rotated at the token's global (t, h, w), the rotated k and the
+// unrotated v written to the cache rows of the slice.
+//
+// GEMM formulation on v_mfma_f32_32x32x16_bf16: C^T = W x^T, so an
+// accumulator block has 32 output features as rows and 32 tokens as columns.
+// In that layout lane l holds token l%32 and features 8(j/4) + 4(l/32) + j%4
+// (j = 0..15): every rotary pair (2p, 2p+1) of a token sits in one lane, and
+// the epilogue rotates it in fp32 straight from the accumulator (no bf16
+// rounding of q and k before the rotation, unlike a projection followed by a
+// separate RoPE kernel).
+//
+// * Workgroup = 8 waves = 256 features x 256 tokens; wave (wf, wt) owns
+//   128 features x 64 tokens (4 x 2 accumulator blocks, 128 VGPRs).
+// * W and x stream through a ring of four LDS stages of 16 K-columns each
+//   (W tile at +0, x tile at +8 KB) with global_load_lds_dwordx4; tile t is
+//   computed while t+1 and t+2 are in flight and t+3 starts into the stage t-1
+//   used.  Loads are branch-free (row and k indices clamped), so the compiler
+//   tracks which stage each load writes.
+// * Both operands are K-contiguous rows (32 B per row per stage) with the
+//   16-byte chunk swizzle c ^ ((row / 8) % 2), which makes the ds_read_b128
+//   fragment reads bank-conflict free; every read is a per-lane base plus an
+//   immediate offset.
+#include "rcc_internal.h"
+
+namespace rcc {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBF = 256;                 // features per workgroup
+constexpr int kBT = 256;                 // tokens per workgroup
+constexpr int kBK = 16;                  // K columns per stage
+constexpr int kRowBytes = kBK * 2;       // 32 B per row per stage
+constexpr int kTileBytes = 256 * kRowBytes;  // 8 KB per operand per stage
+constexpr int kStages = 4;
+constexpr int kXcds = 8;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+struct StagePtrs {
+  char *w0, *x0, *w1, *x1, *w2, *x2, *w3, *x3;
+};
+
+// Wave w loads rows 32 w .. 32 w + 31 of the W tile and of the x tile of
+// K-columns [k0, k0 + 16): lane l -> row 32 w + l/2, LDS chunk slot l%2,
+// global chunk (l%2) ^ ((row / 8) % 2).  Rows past the matrix re-read its
+// last row (their outputs are not stored); k0 past the end re-reads the last
+// K-columns into a stage no step reads again.
+__device__ __forceinline__ void issue_stage(const __bf16* w, const __bf16* x, int f0, int t0,
+                                            int n_feat, int n_tok, int K, int k0, char* ws,
+                                            char* xs, int wave, int lane) {
+  k0 = __builtin_amdgcn_readfirstlane(min(k0, K - kBK));
+  const int r = 32 * wave + (lane >> 1);
+  const int c = (lane & 1) ^ ((r >> 3) & 1);
+  const uint32_t kb = (uint32_t)(k0 * 2 + c * 16);
+  const uint32_t wrow = (uint32_t)min(f0 + r, n_feat - 1);
+  const uint32_t xrow = (uint32_t)min(t0 + r, n_tok - 1);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(w) + (wrow * (uint32_t)(K * 2) + kb),
+                                   (lds_void*)(ws + wave * 1024), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(x) + (xrow * (uint32_t)(K * 2) + kb),
+                                   (lds_void*)(xs + wave * 1024), 16, 0, 0);
+}
+
+// At most n of this wave's loads in flight (2 per stage), then a barrier
+// without a memory fence (a fence would also wait for the later stages).
+template <int n>
+__device__ __forceinline__ void stage_ready() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_ft) {
+  __shared__ __align__(1024) char sS0[2 * kTileBytes];
+  __shared__ __align__(1024) char sS1[2 * kTileBytes];
+  __shared__ __align__(1024) char sS2[2 * kTileBytes];
+  __shared__ __align__(1024) char sS3[2 * kTileBytes];
+  const StagePtrs st{sS0, sS0 + kTileBytes, sS1, sS1 + kTileBytes,
+                     sS2, sS2 + kTileBytes, sS3, sS3 + kTileBytes};
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int wf = wave >> 2;   // 128-feature half
+  const int wt = wave & 3;    // 64-token quarter
+
+  // XCD-major numbering: an XCD's workgroups take consecutive ids, which
+  // walk the feature tiles of one token tile (sharing its x rows in L2).
+  const int total = (int)gridDim.x;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int rem = total % kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int id = xcd * per - (rem && xcd > rem ? xcd - rem : 0) + blockIdx.x / kXcds;
+  const int f0 = (id % n_ft) * kBF;
+  const int t0 = (id / n_ft) * kBT;
+
+  const int K = a.model_dim;
+  const int hd = a.n_heads * a.head_dim;
+  const int n_feat = 3 * hd;
+  const int n_tok = a.batch * a.n_tokens;
+  const __bf16* w = reinterpret_cast<const __bf16*>(a.w);
+  const __bf16* x = reinterpret_cast<const __bf16*>(a.x);
+  const int steps = K / kBK;
+
+  issue_stage(w, x, f0, t0, n_feat, n_tok, K, 0, st.w0, st.x0, wave, lane);
+  issue_stage(w, x, f0, t0, n_feat, n_tok, K, kBK, st.w1, st.x1, wave, lane);
+  issue_stage(w, x, f0, t0, n_feat, n_tok, K, 2 * kBK, st.w2, st.x2, wave, lane);
+
+  const int sw = (g ^ ((l32 >> 3) & 1)) << 4;
+  const int aoff = (wf * 128 + l32) * kRowBytes + sw;
+  const int boff = (wt * 64 + l32) * kRowBytes + sw;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = f32x16{};
+
+  auto step = [&](int t, const char* ws, const char* xs, char* wn, char* xn) {
+    stage_ready<4>();
+    issue_stage(w, x, f0, t0, n_feat, n_tok, K, (t + 3) * kBK, wn, xn, wave, lane);
+    bf16x8 af[4], bfr[2];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) af[fb] = *reinterpret_cast<const bf16x8*>(ws + aoff + fb * 32 * kRowBytes);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const bf16x8*>(xs + boff + tb * 32 * kRowBytes);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma32(af[fb], bfr[tb], acc[fb][tb]);
+  };
+  int t = 0;
+  for (; t + kStages <= steps; t += kStages) {
+    step(t, st.w0, st.x0, st.w3, st.x3);
+    step(t + 1, st.w1, st.x1, st.w0, st.x0);
+    step(t + 2, st.w2, st.x2, st.w1, st.x1);
+    step(t + 3, st.w3, st.x3, st.w2, st.x2);
+  }
+  if (t < steps) step(t, st.w0, st.x0, st.w3, st.x3);
+  if (t + 1 < steps) step(t + 1, st.w1, st.x1, st.w0, st.x0);
+  if (t + 2 < steps) step(t + 2, st.w2, st.x2, st.w1, st.x1);
+  // No load may still be writing this workgroup's LDS when it exits.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // Epilogue: bias, rotation of q and k in fp32, bf16 stores to q_out and the
+  // cache rows.
+  const float2* tab = reinterpret_cast<const float2*>(a.tables);
+  const int64_t row_stride = hd;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int m = t0 + wt * 64 + tb * 32 + l32;
+    if (m >= n_tok) continue;
+    const int b = m / a.n_tokens;
+    const int i = m - b * a.n_tokens;
+    const TokenPos p = token_position(a.grid, i);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
+      if (f >= n_feat) continue;
+      const int which = f / hd;
+      const int fr = f - which * hd;
+      const int head = fr / a.head_dim;
+      const int d0 = fr - head * a.head_dim;
+      __bf16* dst;
+      if (which == 0) {
+        dst = reinterpret_cast<__bf16*>(a.q_out) + ((int64_t)b * a.n_tokens + i) * row_stride;
+      } else {
+        dst = reinterpret_cast<__bf16*>(which == 1 ? a.k_cache : a.v_cache) +
+              ((int64_t)b * a.cache_tokens + p.row) * row_stride;
+      }
+      dst += head * a.head_dim;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int d = d0 + j4 * 8 + g * 4;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[fb][tb][j4 * 4 + e];
+        if (a.bias) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] += a.bias[f + j4 * 8 + g * 4 + e];
+        }
+        if (which < 2) {
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const int pr = (d + e) >> 1;  // rotary pair index inside the head
+            const float2* src;
+            if (pr < a.pt) {
+              src = tab + (int64_t)p.t * a.pt + pr;
+            } else if (pr < a.pt + a.ph) {
+              src = tab + a.off_h + (int64_t)p.h * a.ph + (pr - a.pt);
+            } else {
+              src = tab + a.off_w + (int64_t)p.w * a.pw + (pr - a.pt - a.ph);
+            }
+            const float2 cs = *src;
+            const float x0 = y[e], x1 = y[e + 1];
+            y[e] = x0 * cs.x - x1 * cs.y;
+            y[e + 1] = x0 * cs.y + x1 * cs.x;
+          }
+        }
+        bf16x4 v;
+        v[0] = (__bf16)y[0];
+        v[1] = (__bf16)y[1];
+        v[2] = (__bf16)y[2];
+        v[3] = (__bf16)y[3];
+        *reinterpret_cast<bf16x4*>(dst + d) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_rope_append(const QkvArgs& a, hipStream_t s) {
+  const int n_feat = 3 * a.n_heads * a.head_dim;
+  const int64_t n_tok = (int64_t)a.batch * a.n_tokens;
+  const int n_ft = (n_feat + kBF - 1) / kBF;
+  const int64_t n_tt = (n_tok + kBT - 1) / kBT;
+  hipLaunchKernelGGL(qkv_rope_kernel, dim3((uint32_t)(n_ft * n_tt)), dim3(kThreads), 0, s, a, n_ft);
+  return hipGetLastError();
+}
+
+}  // namespace rcc

@@ -173,6 +173,69 @@ rcc_status rcc_rope3d_apply_append(
                   "rope3d_apply_append launch");
 }
 
+rcc_status rcc_qkv_rope_append(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    int32_t batch, int64_t n_tokens, int32_t n_heads, int32_t model_dim,
+    const void* x, const void* w_qkv, const float* bias,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream) {
+  rcc_status st = check_cfg(cfg);
+  if (st != RCC_OK) return st;
+  rcc::GridArgs g;
+  st = check_grid(grid, n_tokens, &g);
+  if (st != RCC_OK) return st;
+  const int64_t D = (int64_t)cfg->d_t + cfg->d_h + cfg->d_w;
+  if (D % 32) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 32", (long long)D);
+  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
+  if (model_dim <= 0 || model_dim % 16)
+    return fail(RCC_ERR_SHAPE, "model_dim must be a positive multiple of 16 (got %d)", model_dim);
+  const int64_t n_feat = 3 * (int64_t)n_heads * D;
+  const int64_t n_tok = (int64_t)batch * n_tokens;
+  if (n_feat > kI32Max || n_tok > kI32Max) return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
+  // Operand loads use 32-bit byte offsets.
+  if (n_feat * model_dim * 2 > (int64_t)UINT32_MAX || n_tok * model_dim * 2 > (int64_t)UINT32_MAX)
+    return fail(RCC_ERR_SHAPE, "x and w_qkv must each be smaller than 4 GiB");
+  if ((int64_t)grid->start_frame + grid->frames > cfg->max_t)
+    return fail(RCC_ERR_RANGE, "frames [%d, %d) exceed the time table (max_t %d)",
+                grid->start_frame, grid->start_frame + grid->frames, cfg->max_t);
+  if (grid->height > cfg->max_h || grid->width > cfg->max_w)
+    return fail(RCC_ERR_RANGE, "grid %dx%d exceeds the h/w tables (%d, %d)",
+                grid->height, grid->width, cfg->max_h, cfg->max_w);
+  const int64_t last_row = (int64_t)grid->start_frame * g.hw + grid->token_offset + n_tokens;
+  if (last_row > cache_tokens)
+    return fail(RCC_ERR_RANGE, "cache rows up to %lld exceed cache_tokens %lld",
+                (long long)last_row, (long long)cache_tokens);
+  if (n_tokens == 0) return RCC_OK;
+  if (!tables_dev || !x || !w_qkv || !q_out || !k_cache || !v_cache)
+    return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
+  if (!aligned16(tables_dev) || !aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)bias & 3u))
+    return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned (bias 4-byte)");
+
+  rcc::QkvArgs a;
+  a.tables = tables_dev;
+  a.pt = cfg->d_t / 2;
+  a.ph = cfg->d_h / 2;
+  a.pw = cfg->d_w / 2;
+  a.off_h = (int64_t)cfg->max_t * a.pt;
+  a.off_w = a.off_h + (int64_t)cfg->max_h * a.ph;
+  a.grid = g;
+  a.batch = batch;
+  a.n_tokens = (int32_t)n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = (int32_t)D;
+  a.model_dim = model_dim;
+  a.cache_tokens = cache_tokens;
+  a.x = x;
+  a.w = w_qkv;
+  a.bias = bias;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return from_hip(rcc::launch_qkv_rope_append(a, stream), "qkv_rope_append launch");
+}
+
 rcc_status rcc_chunk_causal_attn(
     rcc_dtype in_dtype, rcc_dtype out_dtype,
     int32_t batch, int32_t n_heads, int32_t head_dim,

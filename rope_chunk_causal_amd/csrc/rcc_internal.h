@@ -61,6 +61,22 @@ struct RopeArgs {
 hipError_t launch_rope3d_apply_append(const RopeArgs& a, rcc_dtype in, rcc_dtype out,
                                       hipStream_t s);
 
+struct QkvArgs {
+  const float* tables;
+  int32_t pt, ph, pw;         // pairs per band
+  int64_t off_h, off_w;       // float2 offsets of the h and w tables
+  GridArgs grid;
+  int32_t batch, n_tokens, n_heads, head_dim, model_dim;
+  int64_t cache_tokens;
+  const void* x;              // [batch, n_tokens, model_dim] bf16
+  const void* w;              // [3 * n_heads * head_dim, model_dim] bf16
+  const float* bias;          // [3 * n_heads * head_dim] or nullptr
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+};
+hipError_t launch_qkv_rope_append(const QkvArgs& a, hipStream_t s);
+
 struct AttnArgs {
   int32_t batch, n_heads, head_dim;
   int32_t q_tokens, q_pos, kv_tokens, chunk_tokens;

@@ -116,3 +116,34 @@ def test_positions_and_tables_host_checks():
     assert L.rcc_rope3d_tables(ctypes.byref(bad), FAKE, None) == rcc.RCC_ERR_SHAPE
     good = rcc.rope_cfg(8, 8, 8, 16, 4, 4)
     assert L.rcc_rope3d_tables(ctypes.byref(good), FAKE + 4, None) == rcc.RCC_ERR_ALIGN
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+@pytest.mark.parametrize("kw,status", [
+    (dict(cfg=rcc.rope_cfg(8, 8, 8, 16, 4, 4)), rcc.RCC_ERR_SHAPE),     # D = 24, not 32k
+    (dict(model_dim=40), rcc.RCC_ERR_SHAPE),                            # not 16k
+    (dict(model_dim=0), rcc.RCC_ERR_SHAPE),
+    (dict(batch=0), rcc.RCC_ERR_SHAPE),
+    (dict(nh=0), rcc.RCC_ERR_SHAPE),
+    (dict(n=1 << 20, model_dim=4096), rcc.RCC_ERR_SHAPE),                # x >= 4 GiB
+    (dict(grid=rcc.grid(2, 4, 4, 15, 0)), rcc.RCC_ERR_RANGE),            # s + F > max_t
+    (dict(grid=rcc.grid(2, 4, 4, 0, 1)), rcc.RCC_ERR_RANGE),             # Delta + n > FHW
+    (dict(cache=95), rcc.RCC_ERR_RANGE),
+    (dict(x=0), rcc.RCC_ERR_NULL),
+    (dict(w=FAKE + 8), rcc.RCC_ERR_ALIGN),
+    (dict(bias=FAKE + 2), rcc.RCC_ERR_ALIGN),
+])
+def test_qkv_host_checks(kw, status):
+    a = dict(cfg=rcc.rope_cfg(16, 8, 8, 16, 4, 4), grid=rcc.grid(2, 4, 4, 4, 0), batch=1, n=32,
+             nh=2, model_dim=64, x=FAKE, w=FAKE, bias=None, q_out=FAKE, kc=FAKE, vc=FAKE,
+             cache=96)
+    a.update(kw)
+    if "n" in kw:  # a long slice needs a grid and cache that hold it
+        a["grid"] = rcc.grid(1, 1024, 1024, 0, 0)
+        a["cfg"] = rcc.rope_cfg(16, 8, 8, 16, 1024, 1024)
+        a["cache"] = a["n"]
+    st = rcc.lib().rcc_qkv_rope_append(
+        ctypes.byref(a["cfg"]), FAKE, ctypes.byref(a["grid"]), a["batch"], a["n"], a["nh"],
+        a["model_dim"], a["x"], a["w"], a["bias"], a["q_out"], a["kc"], a["vc"], a["cache"],
+        None)
+    assert st == status, rcc.lib().rcc_last_error()
