@@ -183,7 +183,7 @@ RCC_API rcc_status rcc_chunk_causal_attn(
  * (nearest-even) once, at the store.  q_out gets rotated q; the cache rows
  * of the slice get rotated k and the unrotated v; nothing else is written.
  * Errors: NULL (bias may be NULL); SHAPE (D != d_t + d_h + d_w, D % 32 != 0,
- * model_dim not a positive multiple of 16, batch, n_heads or grid
+ * model_dim not a positive multiple of 32, batch, n_heads or grid
  * non-positive, n_tokens < 0, x or w_qkv of 4 GiB or more); RANGE (as
  * rope3d_apply_append); ALIGN (16 bytes; bias 4 bytes); HIP.
  */

@@ -16,16 +16,19 @@
 // separate RoPE kernel).
 //
 // * Workgroup = 8 waves = 256 features x 256 tokens; wave (wf, wt) owns
-//   128 features x 64 tokens (4 x 2 accumulator blocks, 128 VGPRs).
-// * W and x stream through a ring of four LDS stages of 16 K-columns each
-//   (W tile at +0, x tile at +8 KB) with global_load_lds_dwordx4; tile t is
-//   computed while t+1 and t+2 are in flight and t+3 starts into the stage t-1
-//   used.  Loads are branch-free (row and k indices clamped), so the compiler
-//   tracks which stage each load writes.
-// * Both operands are K-contiguous rows (32 B per row per stage) with the
-//   16-byte chunk swizzle c ^ ((row / 8) % 2), which makes the ds_read_b128
-//   fragment reads bank-conflict free; every read is a per-lane base plus an
-//   immediate offset.
+//   128 features x 64 tokens (4 x 2 accumulator blocks, 128 VGPRs): per
+//   16-deep k-step, 6 fragment reads feed 8 MFMAs.
+// * W and x stream through a ring of four LDS stages of 32 K-columns each
+//   (W tile at +0, x tile at +16 KB; 128 KB) with global_load_lds_dwordx4;
+//   tile t is computed while t+1 and t+2 are in flight and t+3 starts into the
+//   stage t-1 used.  Loads are branch-free (row and k indices clamped), so
+//   the compiler tracks which stage each load writes.
+// * Both operands are K-contiguous rows (64 B per row per stage) with the
+//   16-byte chunk swizzle c ^ ((row / 4) % 4), which makes the ds_read_b128
+//   fragment reads bank-conflict free.
+// * Epilogue: bias and rotation in registers, bf16 results staged through
+//   the (then free) LDS ring so that 16 lanes write each token's 256 B of a
+//   wave's 128 features with one 16-byte store each.
 #include "rcc_internal.h"
 
 namespace rcc {
@@ -36,9 +39,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBF = 256;                 // features per workgroup
 constexpr int kBT = 256;                 // tokens per workgroup
-constexpr int kBK = 16;                  // K columns per stage
-constexpr int kRowBytes = kBK * 2;       // 32 B per row per stage
-constexpr int kTileBytes = 256 * kRowBytes;  // 8 KB per operand per stage
+constexpr int kBK = 32;                  // K columns per stage
+constexpr int kRowBytes = kBK * 2;       // 64 B per row per stage
+constexpr int kTileBytes = 256 * kRowBytes;  // 16 KB per operand per stage
 constexpr int kStages = 4;
 constexpr int kXcds = 8;
 
@@ -53,26 +56,30 @@ struct StagePtrs {
 };
 
 // Wave w loads rows 32 w .. 32 w + 31 of the W tile and of the x tile of
-// K-columns [k0, k0 + 16): lane l -> row 32 w + l/2, LDS chunk slot l%2,
-// global chunk (l%2) ^ ((row / 8) % 2).  Rows past the matrix re-read its
-// last row (their outputs are not stored); k0 past the end re-reads the last
-// K-columns into a stage no step reads again.
+// K-columns [k0, k0 + 32), two instructions of 16 rows each: lane l -> row
+// 32 w + 16 i + l/4, LDS chunk slot l%4, global chunk (l%4) ^ ((row / 4) % 4).
+// Rows past the matrix re-read its last row (their outputs are not stored);
+// k0 past the end re-reads the last K-columns into a stage no step reads
+// again.
 __device__ __forceinline__ void issue_stage(const __bf16* w, const __bf16* x, int f0, int t0,
                                             int n_feat, int n_tok, int K, int k0, char* ws,
                                             char* xs, int wave, int lane) {
   k0 = __builtin_amdgcn_readfirstlane(min(k0, K - kBK));
-  const int r = 32 * wave + (lane >> 1);
-  const int c = (lane & 1) ^ ((r >> 3) & 1);
-  const uint32_t kb = (uint32_t)(k0 * 2 + c * 16);
-  const uint32_t wrow = (uint32_t)min(f0 + r, n_feat - 1);
-  const uint32_t xrow = (uint32_t)min(t0 + r, n_tok - 1);
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(w) + (wrow * (uint32_t)(K * 2) + kb),
-                                   (lds_void*)(ws + wave * 1024), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(x) + (xrow * (uint32_t)(K * 2) + kb),
-                                   (lds_void*)(xs + wave * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 32 * wave + 16 * i + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const uint32_t kb = (uint32_t)(k0 * 2 + c * 16);
+    const uint32_t wrow = (uint32_t)min(f0 + r, n_feat - 1);
+    const uint32_t xrow = (uint32_t)min(t0 + r, n_tok - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(w) + (wrow * (uint32_t)(K * 2) + kb),
+                                     (lds_void*)(ws + (2 * wave + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(x) + (xrow * (uint32_t)(K * 2) + kb),
+                                     (lds_void*)(xs + (2 * wave + i) * 1024), 16, 0, 0);
+  }
 }
 
-// At most n of this wave's loads in flight (2 per stage), then a barrier
+// At most n of this wave's loads in flight (4 per stage), then a barrier
 // without a memory fence (a fence would also wait for the later stages).
 template <int n>
 __device__ __forceinline__ void stage_ready() {
@@ -119,9 +126,11 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   issue_stage(w, x, f0, t0, n_feat, n_tok, K, kBK, st.w1, st.x1, wave, lane);
   issue_stage(w, x, f0, t0, n_feat, n_tok, K, 2 * kBK, st.w2, st.x2, wave, lane);
 
-  const int sw = (g ^ ((l32 >> 3) & 1)) << 4;
-  const int aoff = (wf * 128 + l32) * kRowBytes + sw;
-  const int boff = (wt * 64 + l32) * kRowBytes + sw;
+  // chunk 2 kk + g of row r sits in slot (2 kk + g) ^ ((r / 4) % 4)
+  const int sw0 = (g ^ ((l32 >> 2) & 3)) << 4;
+  const int sw1 = ((2 + g) ^ ((l32 >> 2) & 3)) << 4;
+  const int aoff0 = (wf * 128 + l32) * kRowBytes + sw0, aoff1 = aoff0 - sw0 + sw1;
+  const int boff0 = (wt * 64 + l32) * kRowBytes + sw0, boff1 = boff0 - sw0 + sw1;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -130,17 +139,21 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
     for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = f32x16{};
 
   auto step = [&](int t, const char* ws, const char* xs, char* wn, char* xn) {
-    stage_ready<4>();
+    stage_ready<8>();
     issue_stage(w, x, f0, t0, n_feat, n_tok, K, (t + 3) * kBK, wn, xn, wave, lane);
-    bf16x8 af[4], bfr[2];
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) af[fb] = *reinterpret_cast<const bf16x8*>(ws + aoff + fb * 32 * kRowBytes);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ao = kk ? aoff1 : aoff0, bo = kk ? boff1 : boff0;
+      bf16x8 af[4], bfr[2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const bf16x8*>(xs + boff + tb * 32 * kRowBytes);
+      for (int fb = 0; fb < 4; ++fb) af[fb] = *reinterpret_cast<const bf16x8*>(ws + ao + fb * 32 * kRowBytes);
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
+      for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const bf16x8*>(xs + bo + tb * 32 * kRowBytes);
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma32(af[fb], bfr[tb], acc[fb][tb]);
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma32(af[fb], bfr[tb], acc[fb][tb]);
+    }
   };
   int t = 0;
   for (; t + kStages <= steps; t += kStages) {
@@ -152,36 +165,29 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   if (t < steps) step(t, st.w0, st.x0, st.w3, st.x3);
   if (t + 1 < steps) step(t + 1, st.w1, st.x1, st.w0, st.x0);
   if (t + 2 < steps) step(t + 2, st.w2, st.x2, st.w1, st.x1);
-  // No load may still be writing this workgroup's LDS when it exits.
+  // Every load has landed and every wave is done with the stages: they now
+  // hold the output tiles.
   __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // Epilogue: bias, rotation of q and k in fp32, bf16 stores to q_out and the
-  // cache rows.
+  // Epilogue 1 (registers -> LDS): bias and the rotation of q and k in fp32,
+  // rounded to bf16, into this wave's 64 x 128 output tile (token-major,
+  // 256 B per token; 16-byte chunk c of token t at slot c ^ (t % 16)).
+  char* tile = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1 : (wave >> 1) == 2 ? sS2 : sS3;
+  tile += (wave & 1) * (kTileBytes);
   const float2* tab = reinterpret_cast<const float2*>(a.tables);
-  const int64_t row_stride = hd;
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const int m = t0 + wt * 64 + tb * 32 + l32;
-    if (m >= n_tok) continue;
-    const int b = m / a.n_tokens;
-    const int i = m - b * a.n_tokens;
+    const int tl = tb * 32 + l32;  // token within the wave tile
+    const int m = min(t0 + wt * 64 + tl, n_tok - 1);
+    const int i = m - (m / a.n_tokens) * a.n_tokens;
     const TokenPos p = token_position(a.grid, i);
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
       const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
       if (f >= n_feat) continue;
       const int which = f / hd;
-      const int fr = f - which * hd;
-      const int head = fr / a.head_dim;
-      const int d0 = fr - head * a.head_dim;
-      __bf16* dst;
-      if (which == 0) {
-        dst = reinterpret_cast<__bf16*>(a.q_out) + ((int64_t)b * a.n_tokens + i) * row_stride;
-      } else {
-        dst = reinterpret_cast<__bf16*>(which == 1 ? a.k_cache : a.v_cache) +
-              ((int64_t)b * a.cache_tokens + p.row) * row_stride;
-      }
-      dst += head * a.head_dim;
+      const int d0 = (f - which * hd) % a.head_dim;
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const int d = d0 + j4 * 8 + g * 4;
@@ -215,8 +221,38 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
         v[1] = (__bf16)y[1];
         v[2] = (__bf16)y[2];
         v[3] = (__bf16)y[3];
-        *reinterpret_cast<bf16x4*>(dst + d) = v;
+        const int c = fb * 4 + j4;  // 16-byte chunk of the 128 features
+        *reinterpret_cast<bf16x4*>(tile + tl * 256 + ((c ^ (tl & 15)) << 4) + g * 8) = v;
       }
+    }
+  }
+
+  // Epilogue 2 (LDS -> global): 16 lanes write one token's 256 B, 4 tokens
+  // per instruction.  Chunk c of the wave's features is one 8-feature run of
+  // one head of q, k or v.
+  const int c = lane & 15;
+  const int fc = f0 + wf * 128 + c * 8;
+  if (fc < n_feat) {
+    const int which = fc / hd;
+    const int fr = fc - which * hd;
+    const int head = fr / a.head_dim;
+    const int dcol = head * a.head_dim + (fr - head * a.head_dim);
+    __bf16* base = reinterpret_cast<__bf16*>(which == 0 ? a.q_out : which == 1 ? a.k_cache : a.v_cache);
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int tl = it * 4 + (lane >> 4);
+      const int m = t0 + wt * 64 + tl;
+      if (m >= n_tok) break;
+      const int b = m / a.n_tokens;
+      const int i = m - b * a.n_tokens;
+      int64_t row;
+      if (which == 0) {
+        row = (int64_t)b * a.n_tokens + i;
+      } else {
+        row = (int64_t)b * a.cache_tokens + token_position(a.grid, i).row;
+      }
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(tile + tl * 256 + ((c ^ (tl & 15)) << 4));
+      *reinterpret_cast<bf16x8*>(base + row * hd + dcol) = v;
     }
   }
 }

@@ -188,8 +188,8 @@ rcc_status rcc_qkv_rope_append(
   if (D % 32) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 32", (long long)D);
   if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
   if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
-  if (model_dim <= 0 || model_dim % 16)
-    return fail(RCC_ERR_SHAPE, "model_dim must be a positive multiple of 16 (got %d)", model_dim);
+  if (model_dim <= 0 || model_dim % 32)
+    return fail(RCC_ERR_SHAPE, "model_dim must be a positive multiple of 32 (got %d)", model_dim);
   const int64_t n_feat = 3 * (int64_t)n_heads * D;
   const int64_t n_tok = (int64_t)batch * n_tokens;
   if (n_feat > kI32Max || n_tok > kI32Max) return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");

@@ -121,7 +121,8 @@ def test_positions_and_tables_host_checks():
 @pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
 @pytest.mark.parametrize("kw,status", [
     (dict(cfg=rcc.rope_cfg(8, 8, 8, 16, 4, 4)), rcc.RCC_ERR_SHAPE),     # D = 24, not 32k
-    (dict(model_dim=40), rcc.RCC_ERR_SHAPE),                            # not 16k
+    (dict(model_dim=40), rcc.RCC_ERR_SHAPE),                            # not 32k
+    (dict(model_dim=48), rcc.RCC_ERR_SHAPE),
     (dict(model_dim=0), rcc.RCC_ERR_SHAPE),
     (dict(batch=0), rcc.RCC_ERR_SHAPE),
     (dict(nh=0), rcc.RCC_ERR_SHAPE),

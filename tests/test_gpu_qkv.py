@@ -63,10 +63,10 @@ def _run(B, n, nh, dims, K, F, H, W, s, off, mx, bias, seed, sample=None):
 
 @pytest.mark.parametrize("B,n,nh,dims,K,F,H,W,s,off,bias", [
     (1, 40, 2, (12, 10, 10), 64, 2, 4, 5, 2, 0, False),        # ragged token and feature tiles
-    (3, 100, 2, (12, 10, 10), 48, 2, 10, 10, 4, 37, True),     # tiles span batch entries
+    (3, 100, 2, (12, 10, 10), 64, 2, 10, 10, 4, 37, True),     # tiles span batch entries
     (2, 300, 3, (44, 42, 42), 128, 3, 10, 12, 6, 50, True),    # head_dim 128, several tiles
-    (1, 1, 1, (12, 10, 10), 16, 1, 1, 1, 0, 0, False),          # one token, one K step
-    (1, 257, 4, (16, 8, 8), 176, 2, 16, 16, 0, 0, False),       # K not a multiple of 64
+    (1, 1, 1, (12, 10, 10), 32, 1, 1, 1, 0, 0, False),          # one token, one K step
+    (1, 257, 4, (16, 8, 8), 160, 2, 16, 16, 0, 0, False),       # K not a multiple of 64
 ])
 def test_small_shapes_every_token(B, n, nh, dims, K, F, H, W, s, off, bias):
     _run(B, n, nh, dims, K, F, H, W, s, off, (16, 16, 16), bias, seed=11)
@@ -119,8 +119,8 @@ def test_errors_reported_without_launch():
     t = torch()
     cfg = rcc.rope_cfg(12, 10, 10, 16, 16, 16)
     tables = rcc.rope3d_tables(cfg)
-    x = t.zeros((1, 8, 40), dtype=t.bfloat16, device="cuda")        # model_dim 40: not 16k
-    w = t.zeros((3 * 2 * 32, 40), dtype=t.bfloat16, device="cuda")
+    x = t.zeros((1, 8, 48), dtype=t.bfloat16, device="cuda")        # model_dim 48: not 32k
+    w = t.zeros((3 * 2 * 32, 48), dtype=t.bfloat16, device="cuda")
     qo = t.zeros((1, 8, 2, 32), dtype=t.bfloat16, device="cuda")
     kc = t.zeros((1, 64, 2, 32), dtype=t.bfloat16, device="cuda")
     with pytest.raises(rcc.RccError) as e:
