@@ -176,44 +176,60 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   char* tile = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1 : (wave >> 1) == 2 ? sS2 : sS3;
   tile += (wave & 1) * (kTileBytes);
   const float2* tab = reinterpret_cast<const float2*>(a.tables);
+  TokenPos pos[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const int tl = tb * 32 + l32;  // token within the wave tile
-    const int m = min(t0 + wt * 64 + tl, n_tok - 1);
-    const int i = m - (m / a.n_tokens) * a.n_tokens;
-    const TokenPos p = token_position(a.grid, i);
+    const int m = min(t0 + wt * 64 + tb * 32 + l32, n_tok - 1);
+    pos[tb] = token_position(a.grid, m - (m / a.n_tokens) * a.n_tokens);
+  }
+  // Per 32-feature block, every global load it needs (bias, and cos/sin of
+  // its 8 rotary pairs for both tokens of the lane) is issued before any is
+  // used: one wait per block instead of one memory round trip per pair.
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-      const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
-      if (f >= n_feat) continue;
-      const int which = f / hd;
-      const int d0 = (f - which * hd) % a.head_dim;
+  for (int fb = 0; fb < 4; ++fb) {
+    const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
+    if (f >= n_feat) continue;
+    const int which = f / hd;
+    const int d0 = (f - which * hd) % a.head_dim;
+    f32x4 bias[4];
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int d = d0 + j4 * 8 + g * 4;
-        float y[4];
+    for (int j4 = 0; j4 < 4; ++j4)
+      bias[j4] = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + f + j4 * 8 + g * 4) : f32x4{};
+    float2 cs[2][4][2];
+    if (which < 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[fb][tb][j4 * 4 + e];
-        if (a.bias) {
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] += a.bias[f + j4 * 8 + g * 4 + e];
-        }
-        if (which < 2) {
+        for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const int pr = (d + e) >> 1;  // rotary pair index inside the head
+          for (int e = 0; e < 2; ++e) {
+            const int pr = ((d0 + j4 * 8 + g * 4) >> 1) + e;  // rotary pair inside the head
             const float2* src;
             if (pr < a.pt) {
-              src = tab + (int64_t)p.t * a.pt + pr;
+              src = tab + (int64_t)pos[tb].t * a.pt + pr;
             } else if (pr < a.pt + a.ph) {
-              src = tab + a.off_h + (int64_t)p.h * a.ph + (pr - a.pt);
+              src = tab + a.off_h + (int64_t)pos[tb].h * a.ph + (pr - a.pt);
             } else {
-              src = tab + a.off_w + (int64_t)p.w * a.pw + (pr - a.pt - a.ph);
+              src = tab + a.off_w + (int64_t)pos[tb].w * a.pw + (pr - a.pt - a.ph);
             }
-            const float2 cs = *src;
-            const float x0 = y[e], x1 = y[e + 1];
-            y[e] = x0 * cs.x - x1 * cs.y;
-            y[e + 1] = x0 * cs.y + x1 * cs.x;
+            cs[tb][j4][e] = *src;
+          }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int tl = tb * 32 + l32;  // token within the wave tile
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[fb][tb][j4 * 4 + e] + bias[j4][e];
+        if (which < 2) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float2 c2 = cs[tb][j4][e];
+            const float x0 = y[2 * e], x1 = y[2 * e + 1];
+            y[2 * e] = x0 * c2.x - x1 * c2.y;
+            y[2 * e + 1] = x0 * c2.y + x1 * c2.x;
           }
         }
         bf16x4 v;
