@@ -181,6 +181,7 @@ def main():
     sp_gbps = sp_bytes / (sp_ms * 1e-3) / 1e9
 
     rollout = rollout_480p(rcc, synth, cfg, tables, randn, stream, dev)
+    qkv = qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev)
 
     traffic = read_traffic("chunk_causal_attn_480p_step")
     result = {
@@ -208,6 +209,7 @@ def main():
                               "bytes": sp_bytes, "frac_hbm": round(sp_gbps / PEAK_HBM_GBPS, 4)},
         "tables_once_ms": round(tables_ms, 3),
         "rollout_480p": rollout,
+        "qkv_rope_append": qkv,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -218,6 +220,72 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows, wl, s, kv, scale)
     print(json.dumps(result), flush=True)
+
+
+def _time_events(fn, stream, reps):
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps
+
+
+def qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev):
+    """The fused QKV projection + Causal-RoPE + cache write on the 480P chunk
+    (4680 tokens) and on the 64-chunk SP-rank batch (64 x 585 tokens), model
+    dim 1536 -> 3 x 12 x 128, with the unfused path beside it: three torch
+    (hipBLASLt) projections into contiguous q, k, v, then rope3d_apply_append.
+    Two input sets alternate; HIP events on the launch stream."""
+    import torch
+    wl = synth.WORKLOADS["480p_step"]
+    nh, D = wl.n_heads, wl.head_dim
+    K = nh * D
+    out = {}
+    for name, B, n, s, off in (("480p_chunk", 1, wl.chunk_tokens, wl.start_frames[0], 0),
+                               ("sp_shard_b64", 64, wl.chunk_tokens // synth.SP_DEGREE, 9,
+                                2 * (wl.chunk_tokens // synth.SP_DEGREE))):
+        g = rcc.grid(wl.frames, wl.height, wl.width, s, off)
+        cap = (s + wl.frames) * wl.hw
+        sets = []
+        for _ in range(2):
+            x = randn(B, n, K)
+            w = (randn(3 * nh * D, K).float() / math.sqrt(K)).to(torch.bfloat16)
+            sets.append(dict(x=x, w=w, q=torch.empty(B, n, nh, D, device=dev, dtype=torch.bfloat16),
+                             kc=torch.empty(B, cap, nh, D, device=dev, dtype=torch.bfloat16),
+                             vc=torch.empty(B, cap, nh, D, device=dev, dtype=torch.bfloat16),
+                             yq=torch.empty(B, n, K, device=dev, dtype=torch.bfloat16),
+                             yk=torch.empty(B, n, K, device=dev, dtype=torch.bfloat16),
+                             yv=torch.empty(B, n, K, device=dev, dtype=torch.bfloat16)))
+
+        def fused(i):
+            st = sets[i % 2]
+            rcc.qkv_rope_append(cfg, tables, g, st["x"], st["w"], None, st["q"], st["kc"], st["vc"],
+                                stream=stream)
+
+        def unfused(i):
+            st = sets[i % 2]
+            w = st["w"]
+            torch.matmul(st["x"], w[:K].t(), out=st["yq"])
+            torch.matmul(st["x"], w[K:2 * K].t(), out=st["yk"])
+            torch.matmul(st["x"], w[2 * K:].t(), out=st["yv"])
+            rcc.rope3d_apply_append(cfg, tables, g, st["yq"].view(B, n, nh, D),
+                                    st["yk"].view(B, n, nh, D), st["yv"].view(B, n, nh, D),
+                                    st["q"], st["kc"], st["vc"], stream=stream)
+
+        for i in range(4):
+            fused(i)
+            unfused(i)
+        torch.cuda.synchronize()
+        reps = 20
+        f_ms = _time_events(fused, stream, reps)
+        u_ms = _time_events(unfused, stream, reps)
+        flop = 2.0 * B * n * K * 3 * nh * D
+        out[name] = {"tokens": B * n, "ms": round(f_ms, 4), "tflops": round(flop / f_ms / 1e9, 1),
+                     "unfused_ms": round(u_ms, 4), "flop": flop}
+    return out
 
 
 def rollout_480p(rcc, synth, cfg, tables, randn, stream, dev):

@@ -5,8 +5,10 @@
 WORKLOAD: attn_480p (chunk_causal_attn, 4680 queries over 14040 keys, 12
 heads), attn_720p (10800 over 75600, 40 heads), rope_480p (one 4680-token
 chunk, 12 heads), rope_sp_b64 (585-token rank slice, 64 chunks batched),
-copy (a plain 1 GiB device-to-device copy: the reference for scaling HBM
-byte counters), all (every one of them, in that order).  Inputs are seeded
+qkv_480p / qkv_sp_b64 (qkv_rope_append, model dim 1536 -> 3 x 12 x 128, on
+the same two token sets), copy (a plain 1 GiB device-to-device copy: the
+reference for scaling HBM byte counters), all (every one of them: copy,
+then the others in the order listed).  Inputs are seeded
 N(0,1) bf16 on the device; nothing is checked here (the tests do that).
 """
 from __future__ import annotations
@@ -58,6 +60,29 @@ def rope(name: str, reps: int, gen) -> None:
         rcc.rope3d_apply_append(cfg, tables, g, q, k, v, qo, kc, vc)
 
 
+def qkv(name: str, reps: int, gen) -> None:
+    wl = synth.WORKLOADS["480p_step"]
+    nh, D = wl.n_heads, wl.head_dim
+    K = nh * D
+    if name == "qkv_480p":
+        batch, n, s, off = 1, wl.chunk_tokens, wl.start_frames[0], 0
+    else:
+        n = wl.chunk_tokens // synth.SP_DEGREE
+        batch, s, off = 64, 9, 2 * n
+    r = wl.rope
+    cfg = rcc.rope_cfg(r.d_t, r.d_h, r.d_w, r.max_t, r.max_h, r.max_w, r.theta)
+    tables = rcc.rope3d_tables(cfg)
+    cap = (s + wl.frames) * wl.hw
+    x = _randn(gen, batch, n, K)
+    w = (torch.randn(3 * nh * D, K, generator=gen, device="cuda") / math.sqrt(K)).to(torch.bfloat16)
+    qo = torch.empty(batch, n, nh, D, device="cuda", dtype=torch.bfloat16)
+    kc = torch.empty(batch, cap, nh, D, device="cuda", dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+    g = rcc.grid(wl.frames, wl.height, wl.width, s, off)
+    for _ in range(reps):
+        rcc.qkv_rope_append(cfg, tables, g, x, w, None, qo, kc, vc)
+
+
 def copy(reps: int) -> None:
     a = torch.ones(COPY_BYTES // 2, device="cuda", dtype=torch.bfloat16)
     b = torch.empty_like(a)
@@ -68,19 +93,22 @@ def copy(reps: int) -> None:
 def main() -> None:
     p = argparse.ArgumentParser()
     p.add_argument("workload", choices=["attn_480p", "attn_720p", "rope_480p", "rope_sp_b64",
-                                        "copy", "all"])
+                                        "qkv_480p", "qkv_sp_b64", "copy", "all"])
     p.add_argument("--reps", type=int, default=3)
     a = p.parse_args()
     rcc.lib()
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
-    names = ["copy", "attn_480p", "attn_720p", "rope_480p", "rope_sp_b64"] \
+    names = ["copy", "attn_480p", "attn_720p", "rope_480p", "rope_sp_b64", "qkv_480p",
+             "qkv_sp_b64"] \
         if a.workload == "all" else [a.workload]
     for n in names:
         if n == "copy":
             copy(a.reps)
         elif n.startswith("attn"):
             attn(n, a.reps, gen)
+        elif n.startswith("qkv"):
+            qkv(n, a.reps, gen)
         else:
             rope(n, a.reps, gen)
         torch.cuda.synchronize()
