@@ -23,9 +23,15 @@ section by section:
 * ``qkv``       — the local QKV projection (Algorithm 3 step 1) followed by
                   Causal-RoPE and the cache write: the fusion of §3.4.1
                   item 3.
+* ``ring``      — a rolling-window KV cache (sink frames plus the most
+                  recent window of frames, stored as a ring) indexed by the
+                  global time index, and attention over what it holds
+                  ([YL] §2.1; [SF] §3.2-3.3, §4.3, where [SF] is "Sparse
+                  Forcing: Native Trainable Sparse Attention for Real-time
+                  Autoregressive Diffusion Video Generation").
 
 Every function here is pinned by the ``-m "not gpu"`` tests against facts
 fixed by the pages or by mathematics (closed forms, invariants, brute force
 on tiny inputs, library special cases); none is "parity unpinned".
 """
-from . import rope3d, attention, qkv  # noqa: F401
+from . import rope3d, attention, qkv, ring  # noqa: F401

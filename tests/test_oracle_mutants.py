@@ -10,9 +10,11 @@ import pytest
 
 import test_oracle_attention as TA
 import test_oracle_qkv as TQ
+import test_oracle_ring as TG
 import test_oracle_rope as TR
 from oracle import attention as A
 from oracle import qkv as Q
+from oracle import ring as G
 from oracle import rope3d as R
 
 _orig_token_freqs = R.token_freqs
@@ -106,6 +108,36 @@ def _mut_qkv_no_bias(x, w, bias, nh, d):
     return _orig_project(x, w, None, nh, d)
 
 
+_orig_held = G.held_frames
+_orig_ring_positions = G.positions
+
+
+def _mut_slot_ring_over_sinks(t, sink, window):
+    return np.mod(np.asarray(t, dtype=np.int64), sink + window)
+
+
+def _mut_slot_offset_not_subtracted(t, sink, window):
+    t = np.asarray(t, dtype=np.int64)
+    return np.where(t < sink, t, sink + np.mod(t, window))
+
+
+def _mut_held_one_short(F, s, sink, window):
+    h = _orig_held(F, s, sink, window)
+    end = s + F
+    return h[h != max(sink, end - window)] if end - window >= sink else h
+
+
+def _mut_held_no_sinks(F, s, sink, window):
+    h = _orig_held(F, s, sink, window)
+    return h[h >= sink]
+
+
+def _mut_ring_time_is_slot(F, H, W, s, off, n, sink, window):
+    p = _orig_ring_positions(F, H, W, s, off, n, sink, window).copy()
+    p[:, 0] = p[:, 3] // (H * W)
+    return p
+
+
 ROPE_PINS = [
     (TR.test_rotation_matches_gptj_interleaved_rope_per_band, ((8, 8, 8),)),
     (TR.test_unit_vector_closed_form, ()),
@@ -119,6 +151,14 @@ QKV_PINS = [
     (TQ.test_projection_brute_force, ()),
     (TQ.test_identity_projection, ()),
     (TQ.test_one_hot_row_lands_in_its_slot, (1, 2, 7)),
+]
+
+RING_PINS = [
+    (TG.test_slot_map_and_held_set_match_a_fifo_store, (2, 5, 2)),
+    (TG.test_positions_rows, ()),
+    (TG.test_rolled_rollout_matches_brute_force_over_a_full_cache, (1, 4, 3)),
+    (TG.test_time_shift_moves_slots_not_outputs, ()),
+    (TG.test_sinks_survive_and_memory_is_bounded, ()),
 ]
 
 ATTN_PINS = [
@@ -156,6 +196,18 @@ def test_qkv_mutant_is_caught(monkeypatch, mutant):
     assert any(_fails(fn, *args) for fn, args in QKV_PINS), f"{mutant.__name__} survived"
 
 
+@pytest.mark.parametrize("attr,mutant", [
+    ("frame_slot", _mut_slot_ring_over_sinks),
+    ("frame_slot", _mut_slot_offset_not_subtracted),
+    ("held_frames", _mut_held_one_short),
+    ("held_frames", _mut_held_no_sinks),
+    ("positions", _mut_ring_time_is_slot),
+])
+def test_ring_mutant_is_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(G, attr, mutant)
+    assert any(_fails(fn, *args) for fn, args in RING_PINS), f"{mutant.__name__} survived"
+
+
 def test_unmutated_oracle_passes_every_pin():
-    for fn, args in ROPE_PINS + ATTN_PINS + QKV_PINS:
+    for fn, args in ROPE_PINS + ATTN_PINS + QKV_PINS + RING_PINS:
         assert not _fails(fn, *args), fn.__name__
