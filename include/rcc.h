@@ -194,6 +194,104 @@ RCC_API rcc_status rcc_qkv_rope_append(
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
     hipStream_t stream);
 
+/*
+ * Rolling-window KV cache ([YL] §2.1: Self-Forcing reaches any video length
+ * with a KV cache and a rolling window; [SF] = "Sparse Forcing: Native
+ * Trainable Sparse Attention for Real-time Autoregressive Diffusion Video
+ * Generation", §3.2: a full cache grows without bound, §3.3: a bounded
+ * memory of persistent sink blocks plus a local window of the newest
+ * blocks, §4.3: sink frames under a fixed KV budget).
+ *
+ * The cache keeps global frames 0 .. sink_frames-1 for good and the
+ * window_frames most recent frames after them, in a ring of
+ * (sink_frames + window_frames) * H*W rows per batch entry:
+ *   frame slot(t) = t                                        if t < sink_frames
+ *                 = sink_frames + (t - sink_frames) mod window_frames   otherwise
+ *   token (t, h, w) -> ring row slot(t) * H*W + h*W + w.
+ * Keys keep the rotation of their global time index t; nothing is
+ * re-rotated when a frame leaves.  sink_frames >= 0; window_frames >= the
+ * chunk's frames (a chunk never evicts its own frames).
+ *
+ * Once chunk [s, s+F) is written the ring holds its sink frames below s+F
+ * and the last window_frames frames ending at s+F-1, and these occupy
+ * exactly ring rows [0, min(s+F, sink+window) * H*W): the visible memory is
+ * always a prefix of the ring, so attention over it needs no gather.
+ */
+typedef struct {
+  int32_t sink_frames;
+  int32_t window_frames;
+} rcc_ring;
+
+/*
+ * Ring rows the chunk described by `grid` attends once it is written:
+ * min(s + F, sink + window) * H*W.  Host-only.  Returns -1 if grid or ring
+ * is NULL or invalid (non-positive grid, s < 0, sink < 0,
+ * window < F, or (sink + window) * H*W >= 2^31).
+ */
+RCC_API int64_t rcc_ring_held_tokens(const rcc_grid* grid, const rcc_ring* ring);
+
+/*
+ * ring_positions — rcc_rope3d_positions with the ring row in column 3:
+ * int32 [n_tokens][4] = {t_global, h, w, ring_row}.  A check/debug export.
+ * Errors: as rcc_rope3d_positions, plus NULL ring and SHAPE (sink < 0,
+ * window < F, (sink + window) * H*W >= 2^31).
+ */
+RCC_API rcc_status rcc_ring_positions(const rcc_grid* grid, const rcc_ring* ring,
+                                      int64_t n_tokens, int32_t* thw_dev, hipStream_t stream);
+
+/*
+ * rope3d_apply_append_ring — rcc_rope3d_apply_append writing the ring:
+ * q and k are rotated at their global (t, h, w) exactly as there; the
+ * rotated k and the unrotated v overwrite the ring rows of the slice's
+ * tokens (evicting the frames that held those slots).  k_cache and
+ * v_cache are [batch, cache_tokens, n_heads, D] with
+ * cache_tokens >= (sink + window) * H*W.
+ * Errors: as rcc_rope3d_apply_append, with the RANGE rule on cache rows
+ * replaced by cache_tokens < (sink + window) * H*W; NULL ring; SHAPE
+ * (sink < 0, window < F, ring of 2^31 rows or more).
+ */
+RCC_API rcc_status rcc_rope3d_apply_append_ring(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_ring* ring, rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int64_t n_tokens, int32_t n_heads,
+    const void* q, const void* k, const void* v,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream);
+
+/*
+ * qkv_rope_append_ring — rcc_qkv_rope_append writing the ring rows of the
+ * slice (same projection, rotation and rounding).
+ * Errors: as rcc_qkv_rope_append, with the ring rules of
+ * rcc_rope3d_apply_append_ring.
+ */
+RCC_API rcc_status rcc_qkv_rope_append_ring(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_ring* ring, int32_t batch, int64_t n_tokens, int32_t n_heads,
+    int32_t model_dim, const void* x, const void* w_qkv, const float* bias,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream);
+
+/*
+ * chunk_causal_attn_ring — attention of (a slice of) the chunk described
+ * by `grid` over the memory the ring holds once that chunk is written
+ * ([YL] Algorithm 3 step 6 over [SF] §3.3's bounded memory): every query
+ * sees every held row, i.e. ring rows [0, rcc_ring_held_tokens(grid, ring)).
+ *   q   [batch, q_tokens, n_heads, head_dim], q_tokens <= F*H*W
+ *       (grid->token_offset does not matter here).
+ *   k_cache, v_cache [batch, cache_tokens, n_heads, head_dim].
+ *   out [batch, q_tokens, n_heads, head_dim].
+ * Numerics as rcc_chunk_causal_attn (bf16 matrix-core operands, fp32
+ * softmax and accumulation).  The keys are visited in ring order, not in
+ * global time order; softmax does not depend on the order.
+ * Errors: as rcc_chunk_causal_attn; NULL grid or ring; SHAPE (invalid grid
+ * or ring); RANGE (q_tokens > F*H*W, held rows > cache_tokens).
+ */
+RCC_API rcc_status rcc_chunk_causal_attn_ring(
+    const rcc_grid* grid, const rcc_ring* ring, rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int32_t n_heads, int32_t head_dim, int64_t q_tokens, float scale,
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
+    void* out, hipStream_t stream);
+
 /* Static string naming a status code. */
 RCC_API const char* rcc_status_string(rcc_status s);
 

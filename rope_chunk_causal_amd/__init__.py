@@ -23,6 +23,8 @@ RCC_F32, RCC_BF16 = 0, 1
 
 EXPORTS = ("rcc_rope3d_tables_floats", "rcc_rope3d_tables", "rcc_rope3d_positions",
            "rcc_rope3d_apply_append", "rcc_qkv_rope_append", "rcc_chunk_causal_attn",
+           "rcc_ring_held_tokens", "rcc_ring_positions", "rcc_rope3d_apply_append_ring",
+           "rcc_qkv_rope_append_ring", "rcc_chunk_causal_attn_ring",
            "rcc_status_string", "rcc_last_error")
 
 
@@ -44,12 +46,20 @@ class rcc_grid(ctypes.Structure):
                 ("token_offset", ctypes.c_int64)]
 
 
+class rcc_ring(ctypes.Structure):
+    _fields_ = [("sink_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32)]
+
+
 def rope_cfg(d_t, d_h, d_w, max_t, max_h, max_w, theta=10000.0) -> rcc_rope3d_cfg:
     return rcc_rope3d_cfg(d_t, d_h, d_w, max_t, max_h, max_w, float(theta))
 
 
 def grid(frames, height, width, start_frame, token_offset=0) -> rcc_grid:
     return rcc_grid(frames, height, width, start_frame, token_offset)
+
+
+def ring(sink_frames, window_frames) -> rcc_ring:
+    return rcc_ring(sink_frames, window_frames)
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -65,6 +75,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
     cfgp, gridp = ctypes.POINTER(rcc_rope3d_cfg), ctypes.POINTER(rcc_grid)
+    ringp = ctypes.POINTER(rcc_ring)
     L.rcc_rope3d_tables_floats.argtypes = [cfgp]
     L.rcc_rope3d_tables_floats.restype = I64
     L.rcc_rope3d_tables.argtypes = [cfgp, P, P]
@@ -79,6 +90,19 @@ def lib() -> ctypes.CDLL:
     L.rcc_chunk_causal_attn.argtypes = [ctypes.c_int, ctypes.c_int, I32, I32, I32,
                                         I64, I64, I64, I64, F, P, P, P, I64, P, P]
     L.rcc_chunk_causal_attn.restype = ctypes.c_int
+    L.rcc_ring_held_tokens.argtypes = [gridp, ringp]
+    L.rcc_ring_held_tokens.restype = I64
+    L.rcc_ring_positions.argtypes = [gridp, ringp, I64, P, P]
+    L.rcc_ring_positions.restype = ctypes.c_int
+    L.rcc_rope3d_apply_append_ring.argtypes = [cfgp, P, gridp, ringp, ctypes.c_int, ctypes.c_int,
+                                               I32, I64, I32, P, P, P, P, P, P, I64, P]
+    L.rcc_rope3d_apply_append_ring.restype = ctypes.c_int
+    L.rcc_qkv_rope_append_ring.argtypes = [cfgp, P, gridp, ringp, I32, I64, I32, I32,
+                                           P, P, P, P, P, P, I64, P]
+    L.rcc_qkv_rope_append_ring.restype = ctypes.c_int
+    L.rcc_chunk_causal_attn_ring.argtypes = [gridp, ringp, ctypes.c_int, ctypes.c_int, I32, I32,
+                                             I32, I64, F, P, P, P, I64, P, P]
+    L.rcc_chunk_causal_attn_ring.restype = ctypes.c_int
     L.rcc_status_string.argtypes = [ctypes.c_int]
     L.rcc_status_string.restype = ctypes.c_char_p
     L.rcc_last_error.argtypes = []
@@ -169,9 +193,7 @@ def rope3d_positions(g: rcc_grid, n_tokens: int, thw=None, stream=None):
     return thw
 
 
-def rope3d_apply_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, q, k, v, q_out,
-                        k_cache, v_cache, stream=None) -> None:
-    """q, k, v [B, n, heads, D]; q_out same shape; caches [B, cache_tokens, heads, D]."""
+def _rope_append_args(cfg, tables, q, k, v, q_out, k_cache, v_cache):
     torch = _torch()
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or q_out.shape != q.shape:
         raise ValueError("q, k, v, q_out must share one [B, n, heads, D] shape")
@@ -185,20 +207,31 @@ def rope3d_apply_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, q, k, v, q_out
     cap = k_cache.shape[1]
     numel = B * n * nh * D
     ntab = rope3d_tables_floats(cfg)
-    _check(lib().rcc_rope3d_apply_append(
-        ctypes.byref(cfg), _ptr(tables, "tables", ntab, torch.float32), ctypes.byref(g),
-        _dtype_code(q), _dtype_code(q_out), B, n, nh,
-        _ptr(q, "q", numel), _ptr(k, "k", numel), _ptr(v, "v", numel),
-        _ptr(q_out, "q_out", numel), _ptr(k_cache, "k_cache", B * cap * nh * D),
-        _ptr(v_cache, "v_cache", B * cap * nh * D), cap, _stream(stream)),
-        "rope3d_apply_append")
+    return ((_dtype_code(q), _dtype_code(q_out), B, n, nh,
+             _ptr(q, "q", numel), _ptr(k, "k", numel), _ptr(v, "v", numel),
+             _ptr(q_out, "q_out", numel), _ptr(k_cache, "k_cache", B * cap * nh * D),
+             _ptr(v_cache, "v_cache", B * cap * nh * D), cap),
+            _ptr(tables, "tables", ntab, torch.float32))
 
 
-def qkv_rope_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, x, w_qkv, bias, q_out,
-                    k_cache, v_cache, stream=None) -> None:
-    """x [B, n, model_dim] bf16; w_qkv [3*heads*D, model_dim] bf16; bias fp32
-    [3*heads*D] or None; q_out [B, n, heads, D] bf16; caches [B, cache_tokens,
-    heads, D] bf16."""
+def rope3d_apply_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, q, k, v, q_out,
+                        k_cache, v_cache, stream=None) -> None:
+    """q, k, v [B, n, heads, D]; q_out same shape; caches [B, cache_tokens, heads, D]."""
+    args, tab = _rope_append_args(cfg, tables, q, k, v, q_out, k_cache, v_cache)
+    _check(lib().rcc_rope3d_apply_append(ctypes.byref(cfg), tab, ctypes.byref(g), *args,
+                                         _stream(stream)), "rope3d_apply_append")
+
+
+def rope3d_apply_append_ring(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, r: rcc_ring, q, k, v,
+                             q_out, k_cache, v_cache, stream=None) -> None:
+    """As rope3d_apply_append, writing the rolling-window ring rows of the slice."""
+    args, tab = _rope_append_args(cfg, tables, q, k, v, q_out, k_cache, v_cache)
+    _check(lib().rcc_rope3d_apply_append_ring(ctypes.byref(cfg), tab, ctypes.byref(g),
+                                              ctypes.byref(r), *args, _stream(stream)),
+           "rope3d_apply_append_ring")
+
+
+def _qkv_args(cfg, tables, x, w_qkv, bias, q_out, k_cache, v_cache):
     torch = _torch()
     if x.dim() != 3 or q_out.dim() != 4 or tuple(q_out.shape[:2]) != tuple(x.shape[:2]):
         raise ValueError("x must be [B, n, model_dim] and q_out [B, n, heads, D]")
@@ -217,17 +250,33 @@ def qkv_rope_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, x, w_qkv, bias, q_
         raise TypeError("bias must be float32 [3 * heads * D] or None")
     cap = k_cache.shape[1]
     ntab = rope3d_tables_floats(cfg)
-    _check(lib().rcc_qkv_rope_append(
-        ctypes.byref(cfg), _ptr(tables, "tables", ntab, torch.float32), ctypes.byref(g),
-        B, n, nh, K, _ptr(x, "x", B * n * K), _ptr(w_qkv, "w_qkv", 3 * nh * D * K),
-        _ptr(bias, "bias", 3 * nh * D), _ptr(q_out, "q_out", B * n * nh * D),
-        _ptr(k_cache, "k_cache", B * cap * nh * D), _ptr(v_cache, "v_cache", B * cap * nh * D),
-        cap, _stream(stream)), "qkv_rope_append")
+    return ((B, n, nh, K, _ptr(x, "x", B * n * K), _ptr(w_qkv, "w_qkv", 3 * nh * D * K),
+             _ptr(bias, "bias", 3 * nh * D), _ptr(q_out, "q_out", B * n * nh * D),
+             _ptr(k_cache, "k_cache", B * cap * nh * D),
+             _ptr(v_cache, "v_cache", B * cap * nh * D), cap),
+            _ptr(tables, "tables", ntab, torch.float32))
 
 
-def chunk_causal_attn(q, k_cache, v_cache, out, q_pos: int, kv_tokens: int,
-                      chunk_tokens: int, scale: float, stream=None) -> None:
-    """q [B, Lq, heads, D], caches [B, cache_tokens, heads, D], out like q."""
+def qkv_rope_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, x, w_qkv, bias, q_out,
+                    k_cache, v_cache, stream=None) -> None:
+    """x [B, n, model_dim] bf16; w_qkv [3*heads*D, model_dim] bf16; bias fp32
+    [3*heads*D] or None; q_out [B, n, heads, D] bf16; caches [B, cache_tokens,
+    heads, D] bf16."""
+    args, tab = _qkv_args(cfg, tables, x, w_qkv, bias, q_out, k_cache, v_cache)
+    _check(lib().rcc_qkv_rope_append(ctypes.byref(cfg), tab, ctypes.byref(g), *args,
+                                     _stream(stream)), "qkv_rope_append")
+
+
+def qkv_rope_append_ring(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, r: rcc_ring, x, w_qkv, bias,
+                         q_out, k_cache, v_cache, stream=None) -> None:
+    """As qkv_rope_append, writing the rolling-window ring rows of the slice."""
+    args, tab = _qkv_args(cfg, tables, x, w_qkv, bias, q_out, k_cache, v_cache)
+    _check(lib().rcc_qkv_rope_append_ring(ctypes.byref(cfg), tab, ctypes.byref(g),
+                                          ctypes.byref(r), *args, _stream(stream)),
+           "qkv_rope_append_ring")
+
+
+def _attn_shapes(q, k_cache, v_cache, out):
     if q.dim() != 4 or out.shape != q.shape:
         raise ValueError("q and out must share one [B, Lq, heads, D] shape")
     B, lq, nh, D = q.shape
@@ -236,9 +285,46 @@ def chunk_causal_attn(q, k_cache, v_cache, out, q_pos: int, kv_tokens: int,
         raise ValueError("caches must be [B, cache_tokens, heads, D]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches share in_dtype")
-    cap = k_cache.shape[1]
+    return B, lq, nh, D, k_cache.shape[1]
+
+
+def chunk_causal_attn(q, k_cache, v_cache, out, q_pos: int, kv_tokens: int,
+                      chunk_tokens: int, scale: float, stream=None) -> None:
+    """q [B, Lq, heads, D], caches [B, cache_tokens, heads, D], out like q."""
+    B, lq, nh, D, cap = _attn_shapes(q, k_cache, v_cache, out)
     _check(lib().rcc_chunk_causal_attn(
         _dtype_code(q), _dtype_code(out), B, nh, D, lq, q_pos, kv_tokens, chunk_tokens,
         float(scale), _ptr(q, "q", B * lq * nh * D), _ptr(k_cache, "k_cache", B * cap * nh * D),
         _ptr(v_cache, "v_cache", B * cap * nh * D), cap, _ptr(out, "out", B * lq * nh * D),
         _stream(stream)), "chunk_causal_attn")
+
+
+def ring_held_tokens(g: rcc_grid, r: rcc_ring) -> int:
+    """Ring rows the chunk of `g` attends once written (host only)."""
+    n = lib().rcc_ring_held_tokens(ctypes.byref(g), ctypes.byref(r))
+    if n < 0:
+        raise RccError(RCC_ERR_SHAPE, "ring_held_tokens", "invalid grid or ring")
+    return n
+
+
+def ring_positions(g: rcc_grid, r: rcc_ring, n_tokens: int, thw=None, stream=None):
+    """int32 [n_tokens, 4] = (t_global, h, w, ring_row) from the device function."""
+    torch = _torch()
+    if thw is None:
+        thw = torch.empty((max(n_tokens, 0), 4), dtype=torch.int32, device="cuda")
+    p = _ptr(thw, "thw", 4 * max(n_tokens, 0), torch.int32) if n_tokens > 0 else 0
+    _check(lib().rcc_ring_positions(ctypes.byref(g), ctypes.byref(r), n_tokens, p,
+                                    _stream(stream)), "ring_positions")
+    return thw
+
+
+def chunk_causal_attn_ring(g: rcc_grid, r: rcc_ring, q, k_cache, v_cache, out, scale: float,
+                           stream=None) -> None:
+    """Attention of q (the chunk of `g`, or a slice of it) over every row the
+    ring holds once that chunk is written."""
+    B, lq, nh, D, cap = _attn_shapes(q, k_cache, v_cache, out)
+    _check(lib().rcc_chunk_causal_attn_ring(
+        ctypes.byref(g), ctypes.byref(r), _dtype_code(q), _dtype_code(out), B, nh, D, lq,
+        float(scale), _ptr(q, "q", B * lq * nh * D), _ptr(k_cache, "k_cache", B * cap * nh * D),
+        _ptr(v_cache, "v_cache", B * cap * nh * D), cap, _ptr(out, "out", B * lq * nh * D),
+        _stream(stream)), "chunk_causal_attn_ring")

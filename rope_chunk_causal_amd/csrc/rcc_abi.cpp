@@ -62,7 +62,171 @@ rcc_status check_grid(const rcc_grid* g, int64_t n_tokens, rcc::GridArgs* out) {
   out->hw = (int32_t)hw;
   out->start_frame = g->start_frame;
   out->token_offset = (int32_t)g->token_offset;
+  out->sink = 0;
+  out->window = 0;
   return RCC_OK;
+}
+
+// Ring layout checks; on success fills the ring fields of `out` (whose grid
+// part check_grid has already validated) and the ring's row count.
+rcc_status check_ring(const rcc_grid* g, const rcc_ring* r, rcc::GridArgs* out,
+                      int64_t* ring_rows) {
+  if (!r) return fail(RCC_ERR_NULL, "ring is NULL");
+  if (r->sink_frames < 0) return fail(RCC_ERR_SHAPE, "sink_frames < 0");
+  if (r->window_frames < g->frames)
+    return fail(RCC_ERR_SHAPE, "window_frames %d is smaller than the chunk's %d frames",
+                r->window_frames, g->frames);
+  const int64_t rows = ((int64_t)r->sink_frames + r->window_frames) * out->hw;
+  if (rows > kI32Max) return fail(RCC_ERR_SHAPE, "ring rows must be < 2^31");
+  out->sink = r->sink_frames;
+  out->window = r->window_frames;
+  *ring_rows = rows;
+  return RCC_OK;
+}
+
+// Rows of the ring held once the chunk is written: min(s + F, sink + window) frames.
+int64_t held_rows(const rcc_grid* g, const rcc_ring* r) {
+  const int64_t end = (int64_t)g->start_frame + g->frames;
+  const int64_t cap = (int64_t)r->sink_frames + r->window_frames;
+  return (end < cap ? end : cap) * ((int64_t)g->height * g->width);
+}
+
+rcc_status check_tables_cover(const rcc_rope3d_cfg* cfg, const rcc_grid* grid) {
+  if ((int64_t)grid->start_frame + grid->frames > cfg->max_t)
+    return fail(RCC_ERR_RANGE, "frames [%d, %d) exceed the time table (max_t %d)",
+                grid->start_frame, grid->start_frame + grid->frames, cfg->max_t);
+  if (grid->height > cfg->max_h || grid->width > cfg->max_w)
+    return fail(RCC_ERR_RANGE, "grid %dx%d exceeds the h/w tables (%d, %d)",
+                grid->height, grid->width, cfg->max_h, cfg->max_w);
+  return RCC_OK;
+}
+
+// Cache-row range of a write: the plain cache needs rows up to
+// s*H*W + Delta + n; the ring needs (sink + window) * H*W rows.
+rcc_status check_cache_rows(const rcc_grid* grid, const rcc::GridArgs& g, int64_t n_tokens,
+                            int64_t ring_rows, int64_t cache_tokens) {
+  if (g.window > 0) {
+    if (ring_rows > cache_tokens)
+      return fail(RCC_ERR_RANGE, "the ring needs %lld rows, cache_tokens is %lld",
+                  (long long)ring_rows, (long long)cache_tokens);
+    return RCC_OK;
+  }
+  const int64_t last_row = (int64_t)grid->start_frame * g.hw + grid->token_offset + n_tokens;
+  if (last_row > cache_tokens)
+    return fail(RCC_ERR_RANGE, "cache rows up to %lld exceed cache_tokens %lld",
+                (long long)last_row, (long long)cache_tokens);
+  return RCC_OK;
+}
+
+rcc_status rope_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+                       const rcc_ring* ring, bool use_ring, rcc_dtype in_dtype,
+                       rcc_dtype out_dtype, int32_t batch, int64_t n_tokens, int32_t n_heads,
+                       const void* q, const void* k, const void* v, void* q_out,
+                       void* k_cache, void* v_cache, int64_t cache_tokens,
+                       hipStream_t stream) {
+  rcc_status st = check_cfg(cfg);
+  if (st != RCC_OK) return st;
+  rcc::GridArgs g;
+  st = check_grid(grid, n_tokens, &g);
+  if (st != RCC_OK) return st;
+  int64_t ring_rows = 0;
+  if (use_ring && (st = check_ring(grid, ring, &g, &ring_rows)) != RCC_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(RCC_ERR_DTYPE, "unknown dtype code");
+  const int64_t D = (int64_t)cfg->d_t + cfg->d_h + cfg->d_w;
+  if (D % 8) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 8", (long long)D);
+  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
+  if ((int64_t)n_heads * D > kI32Max || n_tokens * (D / 8) > kI32Max)
+    return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
+  if ((st = check_tables_cover(cfg, grid)) != RCC_OK) return st;
+  if ((st = check_cache_rows(grid, g, n_tokens, ring_rows, cache_tokens)) != RCC_OK) return st;
+  if (n_tokens == 0) return RCC_OK;
+  if (!tables_dev || !q || !k || !v || !q_out || !k_cache || !v_cache)
+    return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
+  if (!aligned16(tables_dev) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (q_out == (const void*)q && in_dtype != out_dtype)
+    return fail(RCC_ERR_DTYPE, "in-place q_out needs in_dtype == out_dtype");
+
+  rcc::RopeArgs a;
+  a.tables = tables_dev;
+  a.pt = cfg->d_t / 2;
+  a.ph = cfg->d_h / 2;
+  a.pw = cfg->d_w / 2;
+  a.off_h = (int64_t)cfg->max_t * a.pt;
+  a.off_w = a.off_h + (int64_t)cfg->max_h * a.ph;
+  a.grid = g;
+  a.batch = batch;
+  a.n_tokens = (int32_t)n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = (int32_t)D;
+  a.cache_tokens = cache_tokens;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return from_hip(rcc::launch_rope3d_apply_append(a, in_dtype, out_dtype, stream),
+                  "rope3d_apply_append launch");
+}
+
+rcc_status qkv_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+                      const rcc_ring* ring, bool use_ring, int32_t batch, int64_t n_tokens,
+                      int32_t n_heads, int32_t model_dim, const void* x, const void* w_qkv,
+                      const float* bias, void* q_out, void* k_cache, void* v_cache,
+                      int64_t cache_tokens, hipStream_t stream) {
+  rcc_status st = check_cfg(cfg);
+  if (st != RCC_OK) return st;
+  rcc::GridArgs g;
+  st = check_grid(grid, n_tokens, &g);
+  if (st != RCC_OK) return st;
+  int64_t ring_rows = 0;
+  if (use_ring && (st = check_ring(grid, ring, &g, &ring_rows)) != RCC_OK) return st;
+  const int64_t D = (int64_t)cfg->d_t + cfg->d_h + cfg->d_w;
+  if (D % 32) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 32", (long long)D);
+  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
+  if (model_dim <= 0 || model_dim % 32)
+    return fail(RCC_ERR_SHAPE, "model_dim must be a positive multiple of 32 (got %d)", model_dim);
+  const int64_t n_feat = 3 * (int64_t)n_heads * D;
+  const int64_t n_tok = (int64_t)batch * n_tokens;
+  if (n_feat > kI32Max || n_tok > kI32Max) return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
+  // Operand loads use 32-bit byte offsets.
+  if (n_feat * model_dim * 2 > (int64_t)UINT32_MAX || n_tok * model_dim * 2 > (int64_t)UINT32_MAX)
+    return fail(RCC_ERR_SHAPE, "x and w_qkv must each be smaller than 4 GiB");
+  if ((st = check_tables_cover(cfg, grid)) != RCC_OK) return st;
+  if ((st = check_cache_rows(grid, g, n_tokens, ring_rows, cache_tokens)) != RCC_OK) return st;
+  if (n_tokens == 0) return RCC_OK;
+  if (!tables_dev || !x || !w_qkv || !q_out || !k_cache || !v_cache)
+    return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
+  if (!aligned16(tables_dev) || !aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)bias & 3u))
+    return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned (bias 4-byte)");
+
+  rcc::QkvArgs a;
+  a.tables = tables_dev;
+  a.pt = cfg->d_t / 2;
+  a.ph = cfg->d_h / 2;
+  a.pw = cfg->d_w / 2;
+  a.off_h = (int64_t)cfg->max_t * a.pt;
+  a.off_w = a.off_h + (int64_t)cfg->max_h * a.ph;
+  a.grid = g;
+  a.batch = batch;
+  a.n_tokens = (int32_t)n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = (int32_t)D;
+  a.model_dim = model_dim;
+  a.cache_tokens = cache_tokens;
+  a.x = x;
+  a.w = w_qkv;
+  a.bias = bias;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return from_hip(rcc::launch_qkv_rope_append(a, stream), "qkv_rope_append launch");
 }
 
 }  // namespace
@@ -111,6 +275,28 @@ rcc_status rcc_rope3d_positions(const rcc_grid* grid, int64_t n_tokens, int32_t*
                   "rope3d_positions launch");
 }
 
+rcc_status rcc_ring_positions(const rcc_grid* grid, const rcc_ring* ring, int64_t n_tokens,
+                              int32_t* thw_dev, hipStream_t stream) {
+  rcc::GridArgs g;
+  rcc_status st = check_grid(grid, n_tokens, &g);
+  if (st != RCC_OK) return st;
+  int64_t ring_rows = 0;
+  if ((st = check_ring(grid, ring, &g, &ring_rows)) != RCC_OK) return st;
+  if (n_tokens == 0) return RCC_OK;
+  if (!thw_dev) return fail(RCC_ERR_NULL, "thw_dev is NULL");
+  if (!aligned16(thw_dev)) return fail(RCC_ERR_ALIGN, "thw_dev not 16-byte aligned");
+  return from_hip(rcc::launch_rope3d_positions(g, (int32_t)n_tokens, thw_dev, stream),
+                  "ring_positions launch");
+}
+
+int64_t rcc_ring_held_tokens(const rcc_grid* grid, const rcc_ring* ring) {
+  rcc::GridArgs g;
+  int64_t ring_rows = 0;
+  if (check_grid(grid, 0, &g) != RCC_OK || check_ring(grid, ring, &g, &ring_rows) != RCC_OK)
+    return -1;
+  return held_rows(grid, ring);
+}
+
 rcc_status rcc_rope3d_apply_append(
     const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
     rcc_dtype in_dtype, rcc_dtype out_dtype,
@@ -118,59 +304,19 @@ rcc_status rcc_rope3d_apply_append(
     const void* q, const void* k, const void* v,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
     hipStream_t stream) {
-  rcc_status st = check_cfg(cfg);
-  if (st != RCC_OK) return st;
-  rcc::GridArgs g;
-  st = check_grid(grid, n_tokens, &g);
-  if (st != RCC_OK) return st;
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(RCC_ERR_DTYPE, "unknown dtype code");
-  const int64_t D = (int64_t)cfg->d_t + cfg->d_h + cfg->d_w;
-  if (D % 8) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 8", (long long)D);
-  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
-  if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
-  if ((int64_t)n_heads * D > kI32Max || n_tokens * (D / 8) > kI32Max)
-    return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
-  if ((int64_t)grid->start_frame + grid->frames > cfg->max_t)
-    return fail(RCC_ERR_RANGE, "frames [%d, %d) exceed the time table (max_t %d)",
-                grid->start_frame, grid->start_frame + grid->frames, cfg->max_t);
-  if (grid->height > cfg->max_h || grid->width > cfg->max_w)
-    return fail(RCC_ERR_RANGE, "grid %dx%d exceeds the h/w tables (%d, %d)",
-                grid->height, grid->width, cfg->max_h, cfg->max_w);
-  const int64_t last_row = (int64_t)grid->start_frame * g.hw + grid->token_offset + n_tokens;
-  if (last_row > cache_tokens)
-    return fail(RCC_ERR_RANGE, "cache rows up to %lld exceed cache_tokens %lld",
-                (long long)last_row, (long long)cache_tokens);
-  if (n_tokens == 0) return RCC_OK;
-  if (!tables_dev || !q || !k || !v || !q_out || !k_cache || !v_cache)
-    return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
-  if (!aligned16(tables_dev) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
-      !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  if (q_out == (const void*)q && in_dtype != out_dtype)
-    return fail(RCC_ERR_DTYPE, "in-place q_out needs in_dtype == out_dtype");
+  return rope_append(cfg, tables_dev, grid, nullptr, false, in_dtype, out_dtype, batch,
+                     n_tokens, n_heads, q, k, v, q_out, k_cache, v_cache, cache_tokens, stream);
+}
 
-  rcc::RopeArgs a;
-  a.tables = tables_dev;
-  a.pt = cfg->d_t / 2;
-  a.ph = cfg->d_h / 2;
-  a.pw = cfg->d_w / 2;
-  a.off_h = (int64_t)cfg->max_t * a.pt;
-  a.off_w = a.off_h + (int64_t)cfg->max_h * a.ph;
-  a.grid = g;
-  a.batch = batch;
-  a.n_tokens = (int32_t)n_tokens;
-  a.n_heads = n_heads;
-  a.head_dim = (int32_t)D;
-  a.cache_tokens = cache_tokens;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.q_out = q_out;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  return from_hip(rcc::launch_rope3d_apply_append(a, in_dtype, out_dtype, stream),
-                  "rope3d_apply_append launch");
+rcc_status rcc_rope3d_apply_append_ring(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_ring* ring, rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int64_t n_tokens, int32_t n_heads,
+    const void* q, const void* k, const void* v,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream) {
+  return rope_append(cfg, tables_dev, grid, ring, true, in_dtype, out_dtype, batch,
+                     n_tokens, n_heads, q, k, v, q_out, k_cache, v_cache, cache_tokens, stream);
 }
 
 rcc_status rcc_qkv_rope_append(
@@ -179,61 +325,18 @@ rcc_status rcc_qkv_rope_append(
     const void* x, const void* w_qkv, const float* bias,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
     hipStream_t stream) {
-  rcc_status st = check_cfg(cfg);
-  if (st != RCC_OK) return st;
-  rcc::GridArgs g;
-  st = check_grid(grid, n_tokens, &g);
-  if (st != RCC_OK) return st;
-  const int64_t D = (int64_t)cfg->d_t + cfg->d_h + cfg->d_w;
-  if (D % 32) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 32", (long long)D);
-  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
-  if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
-  if (model_dim <= 0 || model_dim % 32)
-    return fail(RCC_ERR_SHAPE, "model_dim must be a positive multiple of 32 (got %d)", model_dim);
-  const int64_t n_feat = 3 * (int64_t)n_heads * D;
-  const int64_t n_tok = (int64_t)batch * n_tokens;
-  if (n_feat > kI32Max || n_tok > kI32Max) return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
-  // Operand loads use 32-bit byte offsets.
-  if (n_feat * model_dim * 2 > (int64_t)UINT32_MAX || n_tok * model_dim * 2 > (int64_t)UINT32_MAX)
-    return fail(RCC_ERR_SHAPE, "x and w_qkv must each be smaller than 4 GiB");
-  if ((int64_t)grid->start_frame + grid->frames > cfg->max_t)
-    return fail(RCC_ERR_RANGE, "frames [%d, %d) exceed the time table (max_t %d)",
-                grid->start_frame, grid->start_frame + grid->frames, cfg->max_t);
-  if (grid->height > cfg->max_h || grid->width > cfg->max_w)
-    return fail(RCC_ERR_RANGE, "grid %dx%d exceeds the h/w tables (%d, %d)",
-                grid->height, grid->width, cfg->max_h, cfg->max_w);
-  const int64_t last_row = (int64_t)grid->start_frame * g.hw + grid->token_offset + n_tokens;
-  if (last_row > cache_tokens)
-    return fail(RCC_ERR_RANGE, "cache rows up to %lld exceed cache_tokens %lld",
-                (long long)last_row, (long long)cache_tokens);
-  if (n_tokens == 0) return RCC_OK;
-  if (!tables_dev || !x || !w_qkv || !q_out || !k_cache || !v_cache)
-    return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
-  if (!aligned16(tables_dev) || !aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) ||
-      !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)bias & 3u))
-    return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned (bias 4-byte)");
+  return qkv_append(cfg, tables_dev, grid, nullptr, false, batch, n_tokens, n_heads, model_dim,
+                    x, w_qkv, bias, q_out, k_cache, v_cache, cache_tokens, stream);
+}
 
-  rcc::QkvArgs a;
-  a.tables = tables_dev;
-  a.pt = cfg->d_t / 2;
-  a.ph = cfg->d_h / 2;
-  a.pw = cfg->d_w / 2;
-  a.off_h = (int64_t)cfg->max_t * a.pt;
-  a.off_w = a.off_h + (int64_t)cfg->max_h * a.ph;
-  a.grid = g;
-  a.batch = batch;
-  a.n_tokens = (int32_t)n_tokens;
-  a.n_heads = n_heads;
-  a.head_dim = (int32_t)D;
-  a.model_dim = model_dim;
-  a.cache_tokens = cache_tokens;
-  a.x = x;
-  a.w = w_qkv;
-  a.bias = bias;
-  a.q_out = q_out;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  return from_hip(rcc::launch_qkv_rope_append(a, stream), "qkv_rope_append launch");
+rcc_status rcc_qkv_rope_append_ring(
+    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_ring* ring, int32_t batch, int64_t n_tokens, int32_t n_heads,
+    int32_t model_dim, const void* x, const void* w_qkv, const float* bias,
+    void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
+    hipStream_t stream) {
+  return qkv_append(cfg, tables_dev, grid, ring, true, batch, n_tokens, n_heads, model_dim,
+                    x, w_qkv, bias, q_out, k_cache, v_cache, cache_tokens, stream);
 }
 
 rcc_status rcc_chunk_causal_attn(
@@ -282,6 +385,29 @@ rcc_status rcc_chunk_causal_attn(
   a.out = out;
   return from_hip(rcc::launch_chunk_causal_attn(a, in_dtype, out_dtype, stream),
                   "chunk_causal_attn launch");
+}
+
+rcc_status rcc_chunk_causal_attn_ring(
+    const rcc_grid* grid, const rcc_ring* ring, rcc_dtype in_dtype, rcc_dtype out_dtype,
+    int32_t batch, int32_t n_heads, int32_t head_dim, int64_t q_tokens, float scale,
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
+    void* out, hipStream_t stream) {
+  rcc::GridArgs g;
+  rcc_status st = check_grid(grid, 0, &g);
+  if (st != RCC_OK) return st;
+  int64_t ring_rows = 0;
+  if ((st = check_ring(grid, ring, &g, &ring_rows)) != RCC_OK) return st;
+  const int64_t held = held_rows(grid, ring);
+  if (q_tokens > (int64_t)grid->frames * g.hw)
+    return fail(RCC_ERR_RANGE, "q_tokens %lld exceed the chunk's %lld tokens",
+                (long long)q_tokens, (long long)grid->frames * g.hw);
+  if (held > cache_tokens)
+    return fail(RCC_ERR_RANGE, "the ring holds %lld rows, cache_tokens is %lld",
+                (long long)held, (long long)cache_tokens);
+  // Every query sees every held row, and the held rows are the ring's
+  // prefix [0, held): one key block that all queries share.
+  return rcc_chunk_causal_attn(in_dtype, out_dtype, batch, n_heads, head_dim, q_tokens, 0, held,
+                               held, scale, q, k_cache, v_cache, cache_tokens, out, stream);
 }
 
 }  // extern "C"

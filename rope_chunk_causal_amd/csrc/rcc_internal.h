@@ -15,10 +15,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Position of a call's token inside the video ([YL] §3.3.3).  All values
 // fit in 32 bits: the host checks F*H*W < 2^31 and cache rows < 2^31.
+// window == 0: the cache keeps every frame in global order.  window > 0:
+// a rolling-window ring that keeps frames [0, sink) and the `window` most
+// recent frames (Sparse Forcing §3.3's sink blocks plus local window).
 struct GridArgs {
   int32_t height, width, hw;  // H, W, H*W
   int32_t start_frame;        // s
   int32_t token_offset;       // Delta
+  int32_t sink, window;       // ring layout (window 0 = no ring)
 };
 
 struct TokenPos {
@@ -26,7 +30,9 @@ struct TokenPos {
 };
 
 // i_global = Delta + i; frame in chunk = i_global / HW; t_global = s + frame;
-// h, w in row-major order; cache row = s*HW + i_global.
+// h, w in row-major order.  Cache row = slot(t_global) * HW + h*W + w, with
+// slot(t) = t for the plain cache (so row = s*HW + i_global) and, for the
+// ring, t below the sinks or sink + (t - sink) mod window.
 __device__ __forceinline__ TokenPos token_position(const GridArgs& g, int32_t i) {
   const uint32_t ig = (uint32_t)(g.token_offset + i);
   const uint32_t f = ig / (uint32_t)g.hw;
@@ -36,7 +42,10 @@ __device__ __forceinline__ TokenPos token_position(const GridArgs& g, int32_t i)
   p.t = g.start_frame + (int32_t)f;
   p.h = (int32_t)h;
   p.w = (int32_t)(rem - h * (uint32_t)g.width);
-  p.row = g.start_frame * g.hw + (int32_t)ig;
+  int32_t slot = p.t;
+  if (g.window > 0 && p.t >= g.sink)
+    slot = g.sink + (int32_t)((uint32_t)(p.t - g.sink) % (uint32_t)g.window);
+  p.row = slot * g.hw + (int32_t)rem;
   return p;
 }
 

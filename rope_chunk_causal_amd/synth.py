@@ -104,6 +104,9 @@ class Workload:
     start_frames: the start frame s of every chunk in the rollout; the
     attention step for chunk s sees cache frames [0, s + frames).
     steps: denoising steps per chunk (each re-runs RoPE+append+attention).
+    window_frames > 0: the cache is a rolling-window ring that keeps the
+    first sink_frames frames and the window_frames most recent ones; the
+    step for chunk s then sees min(s + frames, sink + window) frames.
     """
     name: str
     n_heads: int
@@ -116,6 +119,8 @@ class Workload:
     dtype: str
     batch: int = 1
     max_t: int = 1024
+    window_frames: int = 0
+    sink_frames: int = 0
 
     @property
     def hw(self) -> int:
@@ -131,13 +136,22 @@ class Workload:
         return RopeShape(d_t, d_h, d_w, 10000.0, self.max_t,
                          max(self.height, 1), max(self.width, 1))
 
+    def cache_frames(self, start_frame: int) -> int:
+        """Frames the step for chunk start_frame attends."""
+        end = start_frame + self.frames
+        if self.window_frames > 0:
+            return min(end, self.sink_frames + self.window_frames)
+        return end
+
     def cache_tokens(self) -> int:
+        if self.window_frames > 0:
+            return (self.sink_frames + self.window_frames) * self.hw
         return (max(self.start_frames) + self.frames) * self.hw
 
     def attn_flops(self, start_frame: int) -> float:
         """4*Lq*Lk*D*heads over visible pairs (all keys visible in the AR step)."""
         lq = self.chunk_tokens
-        lk = (start_frame + self.frames) * self.hw
+        lk = self.cache_frames(start_frame) * self.hw
         return 4.0 * lq * lk * self.head_dim * self.n_heads * self.batch
 
     def rope_bytes(self, n_tokens: Optional[int] = None, elem: int = 2) -> float:
@@ -158,6 +172,13 @@ WORKLOADS: Dict[str, Workload] = {
     "480p_sp_shard": Workload("480p_sp_shard", 12, 128, 3, 30, 52, [9], 1, "bf16"),
     # Wan-14B-shaped 720P step: 40 heads, chunk at frames 18..20.
     "720p_step": Workload("720p_step", 40, 128, 3, 45, 80, [18], 1, "bf16"),
+    # Long rollouts through a rolling window of 21 latent frames (the 5 s
+    # horizon): 20 s = 81 latent frames in 27 chunks, 1 min = 240 frames in
+    # 80 chunks, 4 denoising steps each.
+    "480p_rolling_20s": Workload("480p_rolling_20s", 12, 128, 3, 30, 52,
+                                 list(range(0, 81, 3)), 4, "bf16", window_frames=21),
+    "480p_rolling_1min": Workload("480p_rolling_1min", 12, 128, 3, 30, 52,
+                                  list(range(0, 240, 3)), 4, "bf16", window_frames=21),
 }
 
 SP_DEGREE = 8  # ranks the 480p_sp_shard workload is split over
@@ -166,6 +187,7 @@ SP_DEGREE = 8  # ranks the 480p_sp_shard workload is split over
 def seed_for(workload: str, start_frame: int, step: int, tensor: str) -> int:
     """Deterministic seed per (workload, chunk, step, tensor)."""
     base = {"tiny": 1, "480p_step": 20, "480p_rollout": 300,
-            "480p_sp_shard": 40, "720p_step": 50}[workload]
-    t = {"q": 0, "k": 1000, "v": 2000, "kc": 3000, "vc": 4000}[tensor]
+            "480p_sp_shard": 40, "720p_step": 50, "480p_rolling_20s": 600,
+            "480p_rolling_1min": 900}[workload]
+    t = {"q": 0, "k": 100000, "v": 200000, "kc": 300000, "vc": 400000}[tensor]
     return base + 10 * start_frame + step + t

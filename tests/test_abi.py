@@ -148,3 +148,78 @@ def test_qkv_host_checks(kw, status):
         a["model_dim"], a["x"], a["w"], a["bias"], a["q_out"], a["kc"], a["vc"], a["cache"],
         None)
     assert st == status, rcc.lib().rcc_last_error()
+
+
+@pytest.mark.parametrize("F,H,W,s,sink,window,held", [
+    (3, 2, 2, 0, 0, 21, 3 * 4),        # first chunk
+    (3, 2, 2, 15, 0, 21, 18 * 4),      # still filling
+    (3, 2, 2, 18, 0, 21, 21 * 4),      # exactly full
+    (3, 2, 2, 99, 0, 21, 21 * 4),      # long after the ring wrapped
+    (2, 3, 5, 0, 1, 4, 2 * 15),
+    (2, 3, 5, 6, 1, 4, 5 * 15),
+])
+def test_ring_held_tokens(F, H, W, s, sink, window, held):
+    assert rcc.ring_held_tokens(rcc.grid(F, H, W, s), rcc.ring(sink, window)) == held
+
+
+def test_ring_held_tokens_rejects_bad_rings():
+    L = rcc.lib()
+    g = rcc.grid(3, 2, 2, 0)
+    for r in (rcc.ring(0, 2), rcc.ring(-1, 5), rcc.ring(1 << 30, 1 << 30)):
+        assert L.rcc_ring_held_tokens(ctypes.byref(g), ctypes.byref(r)) == -1
+    assert L.rcc_ring_held_tokens(ctypes.byref(g), None) == -1
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+@pytest.mark.parametrize("kw,status", [
+    (dict(ring=None), rcc.RCC_ERR_NULL),
+    (dict(ring=rcc.ring(0, 1)), rcc.RCC_ERR_SHAPE),                     # window < F
+    (dict(ring=rcc.ring(-1, 4)), rcc.RCC_ERR_SHAPE),
+    (dict(cache=4 * 16 - 1), rcc.RCC_ERR_RANGE),                        # smaller than the ring
+    (dict(grid=rcc.grid(2, 4, 4, 15, 0)), rcc.RCC_ERR_RANGE),            # s + F > max_t
+    (dict(grid=rcc.grid(2, 4, 4, 0, 1)), rcc.RCC_ERR_RANGE),             # Delta + n > FHW
+    (dict(k=0), rcc.RCC_ERR_NULL),
+    (dict(q=FAKE + 4), rcc.RCC_ERR_ALIGN),
+])
+def test_apply_ring_host_checks(kw, status):
+    # A chunk at frames 12..13 far past a 1-sink 3-window ring: its plain
+    # cache rows would end at 14*16, but the ring needs only 4*16 rows.
+    a = dict(cfg=rcc.rope_cfg(8, 8, 8, 16, 4, 4), grid=rcc.grid(2, 4, 4, 12, 0),
+             ring=rcc.ring(1, 3), q=FAKE, k=FAKE, v=FAKE, cache=4 * 16)
+    a.update(kw)
+    L = rcc.lib()
+    ring = ctypes.byref(a["ring"]) if a["ring"] is not None else None
+    st = L.rcc_rope3d_apply_append_ring(
+        ctypes.byref(a["cfg"]), FAKE, ctypes.byref(a["grid"]), ring, rcc.RCC_F32,
+        rcc.RCC_F32, 1, 32, 2, a["q"], a["k"], a["v"], FAKE + 4096, FAKE, FAKE, a["cache"],
+        None)
+    assert st == status, L.rcc_last_error()
+    if "q" not in kw and "k" not in kw:
+        # the fused projection applies the same ring rules (D = 32 here)
+        cfg = rcc.rope_cfg(16, 8, 8, 16, 4, 4)
+        st = L.rcc_qkv_rope_append_ring(
+            ctypes.byref(cfg), FAKE, ctypes.byref(a["grid"]), ring, 1, 32, 2, 64, FAKE, FAKE,
+            None, FAKE, FAKE, FAKE, a["cache"], None)
+        assert st == status, L.rcc_last_error()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+def test_ring_positions_and_attention_host_checks():
+    L = rcc.lib()
+    g, r = rcc.grid(2, 4, 4, 12, 0), rcc.ring(1, 3)
+    assert L.rcc_ring_positions(ctypes.byref(g), ctypes.byref(r), 33, FAKE, None) == \
+        rcc.RCC_ERR_RANGE
+    assert L.rcc_ring_positions(ctypes.byref(g), None, 8, FAKE, None) == rcc.RCC_ERR_NULL
+    assert L.rcc_ring_positions(ctypes.byref(g), ctypes.byref(r), 0, 0, None) == rcc.RCC_OK
+
+    def attn(grid, ring, q_tokens=32, cache=64, head_dim=24, out=FAKE):
+        return L.rcc_chunk_causal_attn_ring(
+            ctypes.byref(grid), ring and ctypes.byref(ring), rcc.RCC_F32, rcc.RCC_F32, 1, 2,
+            head_dim, q_tokens, 0.2, FAKE, FAKE, FAKE, cache, out, None)
+    assert attn(g, None) == rcc.RCC_ERR_NULL
+    assert attn(g, rcc.ring(0, 1)) == rcc.RCC_ERR_SHAPE
+    assert attn(g, r, q_tokens=33) == rcc.RCC_ERR_RANGE               # more than the chunk
+    assert attn(g, r, cache=63) == rcc.RCC_ERR_RANGE                  # ring holds 64 rows
+    assert attn(g, r, head_dim=20) == rcc.RCC_ERR_SHAPE
+    assert attn(g, r, out=FAKE + 8) == rcc.RCC_ERR_ALIGN
+    assert attn(g, r, q_tokens=0) == rcc.RCC_OK
