@@ -182,6 +182,7 @@ def main():
 
     rollout = rollout_480p(rcc, synth, cfg, tables, randn, stream, dev)
     qkv = qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev)
+    rolling = rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev)
 
     traffic = read_traffic("chunk_causal_attn_480p_step")
     result = {
@@ -210,6 +211,7 @@ def main():
         "tables_once_ms": round(tables_ms, 3),
         "rollout_480p": rollout,
         "qkv_rope_append": qkv,
+        "rolling_1min": rolling,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -335,6 +337,114 @@ def rollout_480p(rcc, synth, cfg, tables, randn, stream, dev):
             "attn_ms": round(attn_ms, 3), "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 1),
             "rope_ms": round(rope_ms, 3), "rope_gbps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
             "attn_flop": flops}
+
+
+def rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev):
+    """One layer of a 1-minute 480P rollout (80 chunks x 4 denoising steps,
+    frames 0..239) through the rolling-window ring of 21 frames, beside the
+    same rollout over a cache that keeps every frame.  Each step is
+    RoPE + append then attention over what the cache holds.  Eight input sets
+    rotate (their content does not change the work); the ring rollout is
+    timed once after an untimed pass, the full-cache one once after a short
+    warm-up; HIP events on the launch stream give the per-kernel sums.
+    Also times the ring write alone on the 64-chunk SP-rank batch."""
+    import torch
+    wl = synth.WORKLOADS["480p_rolling_1min"]
+    nh, D, L, hw, F = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.hw, wl.frames
+    bf = torch.bfloat16
+    sets = [[randn(1, L, nh, D) for _ in range(3)] for _ in range(8)]
+    qo = torch.empty(1, L, nh, D, device=dev, dtype=bf)
+    out = torch.empty_like(qo)
+    scale = 1.0 / math.sqrt(D)
+    steps = [s for s in wl.start_frames for _ in range(wl.steps)]
+    ring = rcc.ring(wl.sink_frames, wl.window_frames)
+
+    def run(kc, vc, use_ring, steps, ev=None):
+        for i, s in enumerate(steps):
+            q, k, v = sets[i % len(sets)]
+            g = rcc.grid(F, wl.height, wl.width, s, 0)
+            if ev is not None:
+                ev[i][0].record(stream)
+            if use_ring:
+                rcc.rope3d_apply_append_ring(cfg, tables, g, ring, q, k, v, qo, kc, vc,
+                                             stream=stream)
+            else:
+                rcc.rope3d_apply_append(cfg, tables, g, q, k, v, qo, kc, vc, stream=stream)
+            if ev is not None:
+                ev[i][1].record(stream)
+            if use_ring:
+                rcc.chunk_causal_attn_ring(g, ring, qo, kc, vc, out, scale, stream=stream)
+            else:
+                rcc.chunk_causal_attn(qo, kc, vc, out, s * hw, (s + F) * hw, L, scale,
+                                      stream=stream)
+            if ev is not None:
+                ev[i][2].record(stream)
+
+    def timed(cap, use_ring, warm_steps):
+        kc = torch.zeros(1, cap, nh, D, device=dev, dtype=bf)
+        vc = torch.zeros_like(kc)
+        run(kc, vc, use_ring, warm_steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(kc, vc, use_ring, steps)
+        torch.cuda.synchronize()
+        total = (time.perf_counter() - t0) * 1e3
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in steps]
+        run(kc, vc, use_ring, steps, ev)
+        torch.cuda.synchronize()
+        rope = [e[0].elapsed_time(e[1]) for e in ev]
+        attn = [e[1].elapsed_time(e[2]) for e in ev]
+        del kc, vc
+        return total, rope, attn
+
+    ring_rows = wl.cache_tokens()
+    r_total, r_rope, r_attn = timed(ring_rows, True, steps)
+    full_rows = (wl.start_frames[-1] + F) * hw
+    f_total, f_rope, f_attn = timed(full_rows, False, steps[:8])
+    torch.cuda.empty_cache()
+
+    def flops(s, ring_kv):
+        lk = min(s + F, wl.sink_frames + wl.window_frames) if ring_kv else s + F
+        return 4.0 * L * lk * hw * D * nh
+    r_flop = sum(flops(s, True) for s in steps)
+    f_flop = sum(flops(s, False) for s in steps)
+    full_from = next(i for i, s in enumerate(steps) if s + F >= wl.sink_frames + wl.window_frames)
+    steady_attn = sum(r_attn[full_from:]) / (len(steps) - full_from)
+    steady_rope = sum(r_rope[full_from:]) / (len(steps) - full_from)
+    rope_bytes = 6.0 * L * nh * D * 2
+
+    # the ring write alone on the SP-rank batch (64 x 585 tokens at frames 237..239)
+    n_sp, B_sp = L // synth.SP_DEGREE, 64
+    g_sp = rcc.grid(F, wl.height, wl.width, 237, 2 * n_sp)
+    sp_sets = [[randn(B_sp, n_sp, nh, D) for _ in range(3)] +
+               [torch.empty(B_sp, n_sp, nh, D, device=dev, dtype=bf),
+                torch.empty(B_sp, ring_rows, nh, D, device=dev, dtype=bf),
+                torch.empty(B_sp, ring_rows, nh, D, device=dev, dtype=bf)] for _ in range(2)]
+
+    def sp_ring(i):
+        rcc.rope3d_apply_append_ring(cfg, tables, g_sp, ring, *sp_sets[i % 2], stream=stream)
+    for i in range(3):
+        sp_ring(i)
+    sp_ms = _time_events(sp_ring, stream, 20)
+    sp_bytes = 6.0 * B_sp * n_sp * nh * D * 2
+    del sp_sets
+    torch.cuda.empty_cache()
+    kv_bytes = 2 * nh * D * 2
+    return {"window_frames": wl.window_frames, "sink_frames": wl.sink_frames,
+            "chunks": len(wl.start_frames), "steps_per_chunk": wl.steps,
+            "ms_total": round(r_total, 2), "ms_per_chunk": round(r_total / len(wl.start_frames), 4),
+            "attn_ms": round(sum(r_attn), 2),
+            "attn_tflops": round(r_flop / (sum(r_attn) * 1e-3) / 1e12, 1),
+            "steady_attn_ms_per_step": round(steady_attn, 4),
+            "steady_rope_ms_per_step": round(steady_rope, 4),
+            "steady_rope_gbps": round(rope_bytes / (steady_rope * 1e-3) / 1e9, 1),
+            "ring_rows": ring_rows, "ring_kv_bytes": ring_rows * kv_bytes,
+            "rope_ring_sp_b64": {"ms": round(sp_ms, 4),
+                                 "gbps": round(sp_bytes / (sp_ms * 1e-3) / 1e9, 1)},
+            "full_cache": {"ms_total": round(f_total, 2), "attn_ms": round(sum(f_attn), 2),
+                           "attn_tflops": round(f_flop / (sum(f_attn) * 1e-3) / 1e12, 1),
+                           "last_attn_ms_per_step": round(f_attn[-1], 4),
+                           "cache_rows": full_rows, "kv_bytes": full_rows * kv_bytes}}
 
 
 def cpu_baseline(rows_per_head, wl, s, kv, scale):

@@ -15,7 +15,8 @@
  *     KV cache     [batch, cache_tokens, n_heads, head_dim]
  *   Tokens of a chunk are flattened in row-major (frame, row, column)
  *   order; cache row r holds the token whose index, counted over all
- *   frames from global frame 0, is r.
+ *   frames from global frame 0, is r (the *_ring calls use the
+ *   rolling-window layout described at rcc_ring instead).
  * - Every tensor pointer must be 16-byte aligned (RCC_ERR_ALIGN).
  * - Arguments are checked on the host before anything is launched; a call
  *   that returns anything but RCC_OK has launched nothing and written

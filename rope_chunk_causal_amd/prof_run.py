@@ -6,7 +6,9 @@ WORKLOAD: attn_480p (chunk_causal_attn, 4680 queries over 14040 keys, 12
 heads), attn_720p (10800 over 75600, 40 heads), rope_480p (one 4680-token
 chunk, 12 heads), rope_sp_b64 (585-token rank slice, 64 chunks batched),
 qkv_480p / qkv_sp_b64 (qkv_rope_append, model dim 1536 -> 3 x 12 x 128, on
-the same two token sets), copy (a plain 1 GiB device-to-device copy: the
+the same two token sets), ring_1min (one layer of a 1-minute rollout, 80
+chunks x 4 steps, RoPE + ring write then attention over a 21-frame rolling
+window), copy (a plain 1 GiB device-to-device copy: the
 reference for scaling HBM byte counters), all (every one of them: copy,
 then the others in the order listed).  Inputs are seeded
 N(0,1) bf16 on the device; nothing is checked here (the tests do that).
@@ -83,6 +85,29 @@ def qkv(name: str, reps: int, gen) -> None:
         rcc.qkv_rope_append(cfg, tables, g, x, w, None, qo, kc, vc)
 
 
+def ring_1min(reps: int, gen) -> None:
+    wl = synth.WORKLOADS["480p_rolling_1min"]
+    nh, D, L, F = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.frames
+    r = wl.rope
+    cfg = rcc.rope_cfg(r.d_t, r.d_h, r.d_w, r.max_t, r.max_h, r.max_w, r.theta)
+    tables = rcc.rope3d_tables(cfg)
+    ring = rcc.ring(wl.sink_frames, wl.window_frames)
+    kc = torch.zeros(1, wl.cache_tokens(), nh, D, device="cuda", dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    sets = [[_randn(gen, 1, L, nh, D) for _ in range(3)] for _ in range(4)]
+    qo = torch.empty(1, L, nh, D, device="cuda", dtype=torch.bfloat16)
+    out = torch.empty_like(qo)
+    i = 0
+    for _ in range(reps):
+        for s in wl.start_frames:
+            g = rcc.grid(F, wl.height, wl.width, s, 0)
+            for _ in range(wl.steps):
+                q, k, v = sets[i % 4]
+                i += 1
+                rcc.rope3d_apply_append_ring(cfg, tables, g, ring, q, k, v, qo, kc, vc)
+                rcc.chunk_causal_attn_ring(g, ring, qo, kc, vc, out, 1 / math.sqrt(D))
+
+
 def copy(reps: int) -> None:
     a = torch.ones(COPY_BYTES // 2, device="cuda", dtype=torch.bfloat16)
     b = torch.empty_like(a)
@@ -93,7 +118,7 @@ def copy(reps: int) -> None:
 def main() -> None:
     p = argparse.ArgumentParser()
     p.add_argument("workload", choices=["attn_480p", "attn_720p", "rope_480p", "rope_sp_b64",
-                                        "qkv_480p", "qkv_sp_b64", "copy", "all"])
+                                        "qkv_480p", "qkv_sp_b64", "ring_1min", "copy", "all"])
     p.add_argument("--reps", type=int, default=3)
     a = p.parse_args()
     rcc.lib()
@@ -109,6 +134,8 @@ def main() -> None:
             attn(n, a.reps, gen)
         elif n.startswith("qkv"):
             qkv(n, a.reps, gen)
+        elif n == "ring_1min":
+            ring_1min(a.reps, gen)
         else:
             rope(n, a.reps, gen)
         torch.cuda.synchronize()
