@@ -29,9 +29,12 @@ section by section:
                   ([YL] §2.1; [SF] §3.2-3.3, §4.3, where [SF] is "Sparse
                   Forcing: Native Trainable Sparse Attention for Real-time
                   Autoregressive Diffusion Video Generation").
+* ``block_sparse`` — attention of each query block over the union of a
+                  persistent block list and its own local block list
+                  ([SF] §3.3-3.4; the selection is an input).
 
 Every function here is pinned by the ``-m "not gpu"`` tests against facts
 fixed by the pages or by mathematics (closed forms, invariants, brute force
 on tiny inputs, library special cases); none is "parity unpinned".
 """
-from . import rope3d, attention, qkv, ring  # noqa: F401
+from . import rope3d, attention, qkv, ring, block_sparse  # noqa: F401

@@ -9,10 +9,12 @@ import numpy as np
 import pytest
 
 import test_oracle_attention as TA
+import test_oracle_block_sparse as TS
 import test_oracle_qkv as TQ
 import test_oracle_ring as TG
 import test_oracle_rope as TR
 from oracle import attention as A
+from oracle import block_sparse as S
 from oracle import qkv as Q
 from oracle import ring as G
 from oracle import rope3d as R
@@ -138,6 +140,28 @@ def _mut_ring_time_is_slot(F, H, W, s, off, n, sink, window):
     return p
 
 
+_orig_key_blocks = S.key_blocks
+_orig_block_sparse = S.block_sparse_attention
+
+
+def _mut_blocks_repeats_kept(persist, local, n_kb):
+    ids = np.concatenate([np.asarray(persist).reshape(-1), np.asarray(local).reshape(-1)])
+    return np.sort(ids[(ids >= 0) & (ids < n_kb)])
+
+
+def _mut_blocks_no_persistent(persist, local, n_kb):
+    return _orig_key_blocks(np.zeros(0, dtype=np.int64), local, n_kb)
+
+
+def _mut_blocks_padding_kept(persist, local, n_kb):
+    ids = np.concatenate([np.asarray(persist).reshape(-1), np.asarray(local).reshape(-1)])
+    return np.unique(ids[ids < n_kb])
+
+
+def _mut_local_of_next_block(q, kc, vc, kv, blk, persist, local, scale):
+    return _orig_block_sparse(q, kc, vc, kv, blk, persist, np.roll(local, 1, axis=2), scale)
+
+
 ROPE_PINS = [
     (TR.test_rotation_matches_gptj_interleaved_rope_per_band, ((8, 8, 8),)),
     (TR.test_unit_vector_closed_form, ()),
@@ -159,6 +183,14 @@ RING_PINS = [
     (TG.test_rolled_rollout_matches_brute_force_over_a_full_cache, (1, 4, 3)),
     (TG.test_time_shift_moves_slots_not_outputs, ()),
     (TG.test_sinks_survive_and_memory_is_bounded, ()),
+]
+
+SPARSE_PINS = [
+    (TS.test_brute_force_tiny, ()),
+    (TS.test_every_block_selected_is_dense_attention, ()),
+    (TS.test_identical_keys_average_v_and_empty_gives_zero, ()),
+    (TS.test_padding_repeats_and_order_change_nothing, ()),
+    (TS.test_persistent_only_is_attention_over_the_gathered_rows, ()),
 ]
 
 ATTN_PINS = [
@@ -208,6 +240,17 @@ def test_ring_mutant_is_caught(monkeypatch, attr, mutant):
     assert any(_fails(fn, *args) for fn, args in RING_PINS), f"{mutant.__name__} survived"
 
 
+@pytest.mark.parametrize("attr,mutant", [
+    ("key_blocks", _mut_blocks_repeats_kept),
+    ("key_blocks", _mut_blocks_no_persistent),
+    ("key_blocks", _mut_blocks_padding_kept),
+    ("block_sparse_attention", _mut_local_of_next_block),
+])
+def test_block_sparse_mutant_is_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(S, attr, mutant)
+    assert any(_fails(fn, *args) for fn, args in SPARSE_PINS), f"{mutant.__name__} survived"
+
+
 def test_unmutated_oracle_passes_every_pin():
-    for fn, args in ROPE_PINS + ATTN_PINS + QKV_PINS + RING_PINS:
+    for fn, args in ROPE_PINS + ATTN_PINS + QKV_PINS + RING_PINS + SPARSE_PINS:
         assert not _fails(fn, *args), fn.__name__
