@@ -293,6 +293,45 @@ RCC_API rcc_status rcc_chunk_causal_attn_ring(
     const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
     void* out, hipStream_t stream);
 
+/*
+ * block_sparse_attn — attention of each query block over a persistent +
+ * local block memory ([SF] §3.3: the memory is the persistent set P, sink
+ * blocks plus blocks kept from history, and the local window L, with
+ * K = [K_P; K_L]; inside the local window each query block keeps its own
+ * Top-K blocks Omega(q); §3.4: one kernel attends every query block to P
+ * and to its Omega(q)).  The selection is an input; choosing it (block
+ * scores, Top-C, Top-K) is the caller's.
+ *   q        bf16 [batch, q_tokens, n_heads, 128], block-contiguous: query
+ *            block i is rows [i*B, (i+1)*B) (the last one may be short).
+ *   k_cache, v_cache bf16 [batch, cache_tokens, n_heads, 128]: key block j
+ *            is rows [j*B, (j+1)*B); blocks j < kv_tokens / B exist.
+ *   persist  int32 [batch, n_heads, n_persist] device: key blocks every
+ *            query block of that (batch, head) attends.
+ *   local    int32 [batch, n_heads, ceil(q_tokens / B), n_local] device:
+ *            the key blocks each query block adds.
+ *   out      [batch, q_tokens, n_heads, 128] in `out_dtype`.
+ * B = block_tokens.  Query block i attends the union of its two lists:
+ * repeated entries count once and entries outside [0, kv_tokens / B)
+ * are ignored (-1 pads a list).  out = softmax(scale * q k^T) v over the
+ * union's keys, fp32 softmax and accumulation, bf16 matrix-core operands;
+ * a query block with an empty union gets zeros.  Keys are visited in
+ * ascending block order whatever the lists' order, so the result does not
+ * depend on it.
+ * Errors: NULL (a tensor, or a list whose length is non-zero); DTYPE
+ * (in_dtype not bf16, unknown out_dtype); SHAPE (head_dim != 128,
+ * block_tokens not 32, 64, 128 or 256, batch/n_heads non-positive,
+ * q_tokens/kv_tokens/n_persist/n_local negative, n_persist + n_local >
+ * 1024, kv_tokens / B > 32768, scale not positive and finite, a batch
+ * entry's cache of 4 GiB or more); RANGE (kv_tokens > cache_tokens);
+ * ALIGN (tensors 16 bytes, lists 4 bytes); HIP.
+ */
+RCC_API rcc_status rcc_block_sparse_attn(
+    rcc_dtype in_dtype, rcc_dtype out_dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
+    int64_t q_tokens, int64_t kv_tokens, int32_t block_tokens, float scale,
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
+    const int32_t* persist, int32_t n_persist, const int32_t* local, int32_t n_local,
+    void* out, hipStream_t stream);
+
 /* Static string naming a status code. */
 RCC_API const char* rcc_status_string(rcc_status s);
 

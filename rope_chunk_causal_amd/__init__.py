@@ -24,7 +24,7 @@ RCC_F32, RCC_BF16 = 0, 1
 EXPORTS = ("rcc_rope3d_tables_floats", "rcc_rope3d_tables", "rcc_rope3d_positions",
            "rcc_rope3d_apply_append", "rcc_qkv_rope_append", "rcc_chunk_causal_attn",
            "rcc_ring_held_tokens", "rcc_ring_positions", "rcc_rope3d_apply_append_ring",
-           "rcc_qkv_rope_append_ring", "rcc_chunk_causal_attn_ring",
+           "rcc_qkv_rope_append_ring", "rcc_chunk_causal_attn_ring", "rcc_block_sparse_attn",
            "rcc_status_string", "rcc_last_error")
 
 
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
     L.rcc_chunk_causal_attn_ring.argtypes = [gridp, ringp, ctypes.c_int, ctypes.c_int, I32, I32,
                                              I32, I64, F, P, P, P, I64, P, P]
     L.rcc_chunk_causal_attn_ring.restype = ctypes.c_int
+    L.rcc_block_sparse_attn.argtypes = [ctypes.c_int, ctypes.c_int, I32, I32, I32, I64, I64, I32,
+                                        F, P, P, P, I64, P, I32, P, I32, P, P]
+    L.rcc_block_sparse_attn.restype = ctypes.c_int
     L.rcc_status_string.argtypes = [ctypes.c_int]
     L.rcc_status_string.restype = ctypes.c_char_p
     L.rcc_last_error.argtypes = []
@@ -328,3 +331,26 @@ def chunk_causal_attn_ring(g: rcc_grid, r: rcc_ring, q, k_cache, v_cache, out, s
         float(scale), _ptr(q, "q", B * lq * nh * D), _ptr(k_cache, "k_cache", B * cap * nh * D),
         _ptr(v_cache, "v_cache", B * cap * nh * D), cap, _ptr(out, "out", B * lq * nh * D),
         _stream(stream)), "chunk_causal_attn_ring")
+
+
+def block_sparse_attn(q, k_cache, v_cache, out, kv_tokens: int, block_tokens: int, persist,
+                      local, scale: float, stream=None) -> None:
+    """q [B, Lq, heads, 128] bf16 (block-contiguous), caches [B, cache_tokens,
+    heads, 128] bf16, out like q (bf16 or fp32); persist int32 [B, heads, n_p]
+    or None; local int32 [B, heads, ceil(Lq / block_tokens), n_l] or None."""
+    torch = _torch()
+    B, lq, nh, D, cap = _attn_shapes(q, k_cache, v_cache, out)
+    n_qb = -(-lq // block_tokens)
+    n_p = 0 if persist is None else persist.shape[-1]
+    n_l = 0 if local is None else local.shape[-1]
+    if persist is not None and tuple(persist.shape) != (B, nh, n_p):
+        raise ValueError("persist must be [B, heads, n_persist]")
+    if local is not None and tuple(local.shape) != (B, nh, n_qb, n_l):
+        raise ValueError("local must be [B, heads, ceil(Lq / block_tokens), n_local]")
+    _check(lib().rcc_block_sparse_attn(
+        _dtype_code(q), _dtype_code(out), B, nh, D, lq, kv_tokens, block_tokens, float(scale),
+        _ptr(q, "q", B * lq * nh * D), _ptr(k_cache, "k_cache", B * cap * nh * D),
+        _ptr(v_cache, "v_cache", B * cap * nh * D), cap,
+        _ptr(persist, "persist", B * nh * n_p, torch.int32) if n_p else 0, n_p,
+        _ptr(local, "local", B * nh * n_qb * n_l, torch.int32) if n_l else 0, n_l,
+        _ptr(out, "out", B * lq * nh * D), _stream(stream)), "block_sparse_attn")

@@ -13,10 +13,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librcc.so")
-SOURCES = ["rcc_abi.cpp", "rope3d.hip", "attn.hip", "attn_d128.hip", "qkv_rope.hip"]
-# The fast attention kernel never relies on NaN semantics (masking uses
+SOURCES = ["rcc_abi.cpp", "rope3d.hip", "attn.hip", "attn_d128.hip", "attn_sparse.hip",
+           "qkv_rope.hip"]
+# The fast attention kernels never rely on NaN semantics (masking uses
 # -inf); without NaN honouring fmaxf needs no quieting of its operands.
-FILE_FLAGS = {"attn_d128.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"attn_d128.hip": ["-fno-honor-nans"], "attn_sparse.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.

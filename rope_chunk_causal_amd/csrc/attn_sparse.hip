@@ -1,0 +1,224 @@
+// Block-sparse attention over a persistent + local block memory, bf16,
+// head_dim 128.
+//
+// [SF] "Sparse Forcing: Native Trainable Sparse Attention for Real-time
+// Autoregressive Diffusion Video Generation", §3.3 (memory M = P u L,
+// K = [K_P; K_L], block-contiguous layout, Top-K blocks Omega(q) per query
+// block inside the local window) and §3.4 (one kernel that attends each
+// query block to the persistent blocks and its own local blocks).  The
+// selection is an input: the persistent list per (batch, head), the local
+// list per (batch, head, query block).
+//
+// Design for gfx950:
+// * One workgroup per (batch, head, query block) of B = 32 * NW rows; wave w
+//   owns query rows 32 w .. 32 w + 31 of the block (NW waves).  The per-tile
+//   work (MFMA S^T and O^T, swizzled LDS, online softmax) is attn_tile.h's.
+// * Setup: the block's key set, the union of its two lists, is built in LDS
+//   as a bitmap over key blocks (LDS atomics; repeats and entries outside
+//   [0, kv_tokens / B) drop out), then compacted in ascending block order
+//   into a visit list with a wave-level scan.  Ascending order makes the
+//   summation order, and so the result, independent of how the lists are
+//   ordered or padded.
+// * Because B is a multiple of the 32-key tile, every tile lies inside one
+//   key block: tile t reads rows list[t / NW] * B + 32 (t % NW) + [0, 32).
+//   There are no partial tiles and no masking; the DMA is the dense
+//   kernel's, with the row base taken from the visit list.
+// * K/V tiles stream global -> LDS with global_load_lds_dwordx4 through a
+//   ring of S stages (S - 1 tiles in flight).  Several workgroups share a CU
+//   (two waves per SIMD at NW = 2 and S = 2), so one workgroup's wait for a
+//   tile is covered by the others' MFMAs.
+// * Workgroups are numbered XCD-major: the query blocks of one head run on
+//   one XCD, whose L2 then serves the persistent blocks every one of them
+//   reads and the local blocks neighbouring query blocks share.
+#include "attn_tile.h"
+
+namespace rcc {
+
+namespace {
+
+using namespace attn128;
+
+constexpr int kMaxSel = 1024;  // list entries per query block (persistent + local)
+
+template <int NW, int S>
+struct Sparse {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kInstr = 8 / NW;      // DMA instructions per wave per tensor per tile
+  static constexpr int kWait = (S - 2) * 2 * kInstr;  // loads of tiles t+1 .. t+S-2
+  static_assert(NW == 1 || NW == 2 || NW == 4 || NW == 8, "block of 32, 64, 128 or 256 rows");
+  static_assert(S >= 2 && S <= 4, "two to four stages");
+};
+
+// Issue this wave's share of tile t (clamped to the last tile: the pipeline
+// runs S - 1 tiles ahead and re-reads the last one into a stage no step reads
+// again).  Instruction i moves key rows 4 i .. 4 i + 3 of the tile into LDS
+// bytes [i KB, +1 KB); lane -> (row 4 i + lane/16, chunk slot lane%16).
+template <int NW>
+__device__ __forceinline__ void issue_sparse(const char* kg, const char* vg, uint32_t row_bytes,
+                                             const int* list, int t, int n_tiles, char* ks,
+                                             char* vs, int wave, int lane) {
+  constexpr int kInstr = 8 / NW;
+  t = __builtin_amdgcn_readfirstlane(min(t, n_tiles - 1));
+  const int blk = __builtin_amdgcn_readfirstlane(list[t / NW]);
+  const uint32_t row0 = (uint32_t)(blk * (32 * NW) + (t % NW) * 32);
+#pragma unroll
+  for (int j = 0; j < kInstr; ++j) {
+    const int i = wave + NW * j;
+    const int r = 4 * i + (lane >> 4);
+    const uint32_t off = (row0 + (uint32_t)r) * row_bytes;
+    __builtin_amdgcn_global_load_lds(kg + (off + k_chunk(r, lane & 15)),
+                                     (lds_void*)(ks + i * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vg + (off + v_chunk(r, lane & 15)),
+                                     (lds_void*)(vs + i * 1024), 16, 0, 0);
+  }
+}
+
+template <typename Tout, int NW, int S>
+__global__ __launch_bounds__(64 * NW, NW > 1 ? 2 : 1) void attn_sparse_kernel(SparseArgs a) {
+  using P = Sparse<NW, S>;
+  // One object per stage (K tile at +0, V at +8 KB), so the compiler does not
+  // order a stage's LDS reads after another stage's DMA writes.
+  __shared__ __align__(1024) char sS0[2 * kTileBytes];
+  __shared__ __align__(1024) char sS1[2 * kTileBytes];
+  __shared__ __align__(1024) char sS2[S > 2 ? 2 * kTileBytes : 16];
+  __shared__ __align__(1024) char sS3[S > 3 ? 2 * kTileBytes : 16];
+  __shared__ int s_list[kMaxSel];
+  __shared__ int s_wave_total[NW];
+  auto stage = [&](int u) -> char* {
+    return u == 0 ? sS0 : u == 1 ? sS1 : u == 2 ? sS2 : sS3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int id = xcd_major_id();
+  const int qb = id % a.n_qblocks;
+  const int bh = id / a.n_qblocks;
+  const int h = bh % a.n_heads;
+  const int b = bh / a.n_heads;
+
+  const int64_t rs = (int64_t)a.n_heads * kD;
+  const __bf16* qg = reinterpret_cast<const __bf16*>(a.q) + (int64_t)b * a.q_tokens * rs + h * kD;
+  const char* kg = reinterpret_cast<const char*>(
+      reinterpret_cast<const __bf16*>(a.k) + (int64_t)b * a.cache_tokens * rs + h * kD);
+  const char* vg = reinterpret_cast<const char*>(
+      reinterpret_cast<const __bf16*>(a.v) + (int64_t)b * a.cache_tokens * rs + h * kD);
+  Tout* og = reinterpret_cast<Tout*>(a.out) + (int64_t)b * a.q_tokens * rs + h * kD;
+
+  const int qrow = qb * (32 * NW) + wave * 32 + l32;
+  const int qclamp = qrow < a.q_tokens ? qrow : a.q_tokens - 1;
+  bf16x8 qf[8];
+  load_q(qf, qg, rs, qclamp, g);
+
+  // ---- the query block's key set: bitmap over key blocks, then compaction
+  uint32_t* bm = reinterpret_cast<uint32_t*>(sS0);
+  const int words = (a.n_kblocks + 31) >> 5;
+  for (int i = tid; i < words; i += P::kThreads) bm[i] = 0u;
+  __syncthreads();
+  const int* pl = a.persist + (int64_t)bh * a.n_persist;
+  const int* ll = a.local + ((int64_t)bh * a.n_qblocks + qb) * a.n_local;
+  const int n_entries = a.n_persist + a.n_local;
+  for (int e = tid; e < n_entries; e += P::kThreads) {
+    const int x = e < a.n_persist ? pl[e] : ll[e - a.n_persist];
+    if ((unsigned)x < (unsigned)a.n_kblocks) atomicOr(&bm[x >> 5], 1u << (x & 31));
+  }
+  __syncthreads();
+  const int wpt = (words + P::kThreads - 1) / P::kThreads;  // words per thread
+  const int w0 = tid * wpt;
+  int cnt = 0;
+  for (int i = 0; i < wpt; ++i)
+    if (w0 + i < words) cnt += __popc(bm[w0 + i]);
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_wave_total[wave] = incl;
+  __syncthreads();
+  int pos = incl - cnt, n_sel = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; ++w2) {
+    const int tot = s_wave_total[w2];
+    pos += w2 < wave ? tot : 0;
+    n_sel += tot;
+  }
+  for (int i = 0; i < wpt; ++i) {
+    if (w0 + i >= words) break;
+    uint32_t word = bm[w0 + i];
+    while (word) {
+      const int bit = __builtin_ctz(word);
+      s_list[pos++] = (w0 + i) * 32 + bit;
+      word &= word - 1u;
+    }
+  }
+  __syncthreads();  // visit list complete; the bitmap's stage is free again
+  n_sel = __builtin_amdgcn_readfirstlane(n_sel);
+  const int n_tiles = n_sel * NW;
+
+  Lane L;
+  lane_setup(L, lane);
+  WaveState w;
+  wave_init(w);
+  const float c2 = a.scale_log2;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u)
+      issue_sparse<NW>(kg, vg, row_bytes, s_list, u, n_tiles, stage(u), stage(u) + kTileBytes,
+                       wave, lane);
+    // Tile t lives in stage t % S; tile t + S - 1 starts into the stage that
+    // tile t - 1 used once every wave is past tile t - 1.
+    auto step = [&](int t, int u) {
+      tile_ready<P::kWait>();
+      const int un = (u + S - 1) % S;
+      issue_sparse<NW>(kg, vg, row_bytes, s_list, t + S - 1, n_tiles, stage(un),
+                       stage(un) + kTileBytes, wave, lane);
+      tile_step<false>(w, L, qf, stage(u), stage(u) + kTileBytes, 0, 0, c2);
+    };
+    int t = 0;
+    for (; t + S <= n_tiles; t += S) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) step(t + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u)
+      if (t + u < n_tiles) step(t + u, u);
+    // No load may still be writing this workgroup's LDS when it exits.
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  if (qrow < a.q_tokens) store_row(w, og + (int64_t)qrow * rs, g);
+}
+
+template <typename Tout, int NW, int S>
+hipError_t launch_nw(const SparseArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.n_qblocks * a.n_heads * a.batch;
+  hipLaunchKernelGGL((attn_sparse_kernel<Tout, NW, S>), dim3((uint32_t)total), dim3(64 * NW), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <typename Tout>
+hipError_t launch_t(const SparseArgs& a, hipStream_t s) {
+  switch (a.block_tokens) {
+    case 32: return launch_nw<Tout, 1, 2>(a, s);
+    case 64: return launch_nw<Tout, 2, 2>(a, s);
+    case 128: return launch_nw<Tout, 4, 2>(a, s);
+    default: return launch_nw<Tout, 8, 4>(a, s);
+  }
+}
+
+}  // namespace
+
+int block_sparse_max_entries() { return kMaxSel; }
+
+hipError_t launch_block_sparse_attn(const SparseArgs& a, rcc_dtype out, hipStream_t s) {
+  return out == RCC_BF16 ? launch_t<__bf16>(a, s) : launch_t<float>(a, s);
+}
+
+}  // namespace rcc

@@ -1,0 +1,221 @@
+// Per-tile machinery of the bf16 / head_dim-128 attention kernels
+// (attn_d128.hip: chunk-causal over a contiguous key range;
+// attn_sparse.hip: block-sparse over a list of key blocks).
+//
+// Formulation: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16; a
+// wave owns 32 query rows, P^T stays in registers, online softmax in base 2
+// with lazy rescaling.  K/V tiles are 32 keys x 256 B, row-major in LDS with
+// an XOR swizzle of the 16-byte chunk index per use, so every LDS read is
+// bank-conflict free: K chunk c of key r sits at c ^ (r % 16) (ds_read_b128
+// of 16 keys at one chunk), V chunk c at c ^ 4 (r % 4) (ds_read_b64_tr_b16
+// of 4 keys x 64 B).  V^T operands come from ds_read_b64_tr_b16: in each
+// 16-lane group, lane i receives element i%4 of the 8-byte chunk addressed by
+// lane 4e + i/4, so 16 lanes that address a 4-key x 16-dim block get that
+// block transposed.  Lazy rescaling: a row's reference max moves only when
+// the tile max exceeds it by more than 2^8; P stays <= 256 and the final
+// O / l is exact.
+#pragma once
+
+#include "rcc_internal.h"
+
+namespace rcc {
+namespace attn128 {
+
+constexpr int kD = 128;
+constexpr int kBN = 32;                      // keys per tile
+constexpr int kRowBytes = kD * 2;            // 256 B per key row
+constexpr int kTileBytes = kBN * kRowBytes;  // 8 KB
+constexpr int kXcds = 8;
+constexpr float kLazy = 8.0f;                // log2 headroom before a rescale
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Global byte offset, inside its key row, of the 16-byte chunk that a DMA
+// lane moves so that LDS chunk slot `cpos` of tile row r holds the swizzled
+// chunk (K: slot c ^ (r % 16); V: slot c ^ 4 (r % 4)).
+__device__ __forceinline__ uint32_t k_chunk(int r, int cpos) {
+  return (uint32_t)((cpos ^ (r & 15)) << 4);
+}
+__device__ __forceinline__ uint32_t v_chunk(int r, int cpos) {
+  return (uint32_t)((cpos ^ ((r & 3) << 2)) << 4);
+}
+
+// Wait until at most n of this wave's DMA instructions are in flight, then a
+// workgroup barrier.  The barrier carries no memory fence: a fence would also
+// wait for the later tiles' loads.
+template <int n>
+__device__ __forceinline__ void tile_ready() {
+  static_assert(n >= 0 && n < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Per-wave state carried across key tiles.
+struct WaveState {
+  f32x16 oacc[4];
+  float m_run, l_run;
+};
+
+// Per-lane constants.
+struct Lane {
+  int koff[8];      // K-fragment byte offsets in a tile
+  int voff[4];      // V^T-fragment byte offsets in a tile (+ kq*16 rows, +8 rows)
+  int g, lim;
+};
+
+__device__ __forceinline__ void lane_setup(Lane& L, int lane) {
+  const int l32 = lane & 31;
+  L.g = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) L.koff[kk] = l32 * kRowBytes + (((kk * 2 + L.g) ^ (l32 & 15)) << 4);
+  const int G = lane >> 4, j = lane & 15;
+  const int vrow = (G >> 1) * 4 + (j >> 2);
+  const int vsw = (j >> 2) << 2;  // 4 * (row % 4)
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int c = dt * 4 + 2 * (G & 1) + ((j & 3) >> 1);
+    L.voff[dt] = vrow * kRowBytes + ((c ^ vsw) << 4) + ((j & 1) << 3);
+  }
+}
+
+__device__ __forceinline__ void wave_init(WaveState& w) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) w.oacc[dt] = f32x16{};
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
+}
+
+// Q^T operand fragments of query row `qrow` (the lane's column of S^T).
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[8], const __bf16* qg, int64_t rs, int qrow,
+                                       int g) {
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qrow * rs + kk * 16 + g * 8);
+}
+
+// One 32-key tile read from stage buffers (ks, vs); later tiles are already
+// being loaded into other stages.  Each stage is a distinct __shared__ object,
+// so the compiler does not order these LDS reads after the other stages' DMA
+// writes.  kMask: keys at or past L.lim get no weight (only tiles that reach
+// lim_lo test it).
+template <bool kMask>
+__device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf16x8 (&qf)[8],
+                                          const char* ks, const char* vs, int j0, int lim_lo,
+                                          float c2) {
+  // S^T = K Q^T, fragment reads kept ahead of the MFMAs that consume them.
+  f32x16 s0 = f32x16{};
+  bf16x8 ka[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const bf16x8*>(ks + L.koff[kk]);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) s0 = mfma32(ka[kk], qf[kk], s0);
+
+  if constexpr (kMask) {
+    if (j0 + kBN > lim_lo) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + (r >> 2) * 8 + L.g * 4 + (r & 3);
+        s0[r] = key < L.lim ? s0[r] : -INFINITY;
+      }
+    }
+  }
+
+  auto vread = [&](int kq, int dt) {
+    const int base = kq * 16 * kRowBytes + L.voff[dt];
+    // Whole-vector form: building the operand element by element from the
+    // v4i16 variant was mis-packed by the compiler.
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vs + base));
+    const bf16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vs + base + 8 * kRowBytes));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  bf16x8 vf[2][4];
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vf[kq][dt] = vread(kq, dt);
+
+  float mx = s0[0];
+#pragma unroll
+  for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);  // v_max3_f32
+  mx = fmaxf(mx, s0[15]);
+  mx = xhalf_max(mx) * c2;
+  // Lazy rescale: move the reference max only when it would grow by > 2^8.
+  const float m_use = (mx - w.m_run > kLazy) ? mx : w.m_run;
+  if (__ballot(m_use != w.m_run)) {
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
+    w.l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
+    w.m_run = m_use;
+  }
+
+  float rsum = 0.f;
+  bf16x8 pf[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -w.m_run));
+    rsum += p;
+    pf[r >> 3][r & 7] = (__bf16)p;
+  }
+  w.l_run += xhalf_sum(rsum);
+
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) w.oacc[dt] = mfma32(vf[kq][dt], pf[kq], w.oacc[dt]);
+}
+
+// O / l for the lane's query row (column of O^T), stored to orow.  A row that
+// saw no key (l = 0) is written as zeros.
+template <typename Tout>
+__device__ __forceinline__ void store_row(const WaveState& w, Tout* orow, int g) {
+  const float inv = w.l_run > 0.f ? 1.f / w.l_run : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const int d0 = dt * 32 + jq * 8 + g * 4;
+      const float x0 = w.oacc[dt][jq * 4] * inv, x1 = w.oacc[dt][jq * 4 + 1] * inv;
+      const float x2 = w.oacc[dt][jq * 4 + 2] * inv, x3 = w.oacc[dt][jq * 4 + 3] * inv;
+      if constexpr (sizeof(Tout) == 2) {
+        bf16x4 v;
+        v[0] = (__bf16)x0; v[1] = (__bf16)x1; v[2] = (__bf16)x2; v[3] = (__bf16)x3;
+        *reinterpret_cast<bf16x4*>(orow + d0) = v;
+      } else {
+        *reinterpret_cast<float4*>(orow + d0) = make_float4(x0, x1, x2, x3);
+      }
+    }
+}
+
+// XCD-aware renumbering of a 1-D grid: dispatch is round-robin over the 8
+// XCDs, so consecutive ids of the result land on one XCD and share its L2.
+__device__ __forceinline__ int xcd_major_id() {
+  const int total = (int)gridDim.x;
+  const int bid = blockIdx.x;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int rem = total % kXcds;
+  const int xcd = bid % kXcds;
+  return xcd * per - (rem && xcd > rem ? xcd - rem : 0) + bid / kXcds;
+}
+
+}  // namespace attn128
+}  // namespace rcc

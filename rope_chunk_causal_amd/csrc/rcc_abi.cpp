@@ -410,4 +410,63 @@ rcc_status rcc_chunk_causal_attn_ring(
                                held, scale, q, k_cache, v_cache, cache_tokens, out, stream);
 }
 
+rcc_status rcc_block_sparse_attn(
+    rcc_dtype in_dtype, rcc_dtype out_dtype, int32_t batch, int32_t n_heads, int32_t head_dim,
+    int64_t q_tokens, int64_t kv_tokens, int32_t block_tokens, float scale,
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_tokens,
+    const int32_t* persist, int32_t n_persist, const int32_t* local, int32_t n_local,
+    void* out, hipStream_t stream) {
+  if (in_dtype != RCC_BF16 || !valid_dtype(out_dtype))
+    return fail(RCC_ERR_DTYPE, "block-sparse attention takes bf16 inputs");
+  if (head_dim != 128) return fail(RCC_ERR_SHAPE, "head_dim must be 128 (got %d)", head_dim);
+  if (block_tokens != 32 && block_tokens != 64 && block_tokens != 128 && block_tokens != 256)
+    return fail(RCC_ERR_SHAPE, "block_tokens must be 32, 64, 128 or 256 (got %d)", block_tokens);
+  if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (n_heads <= 0 || n_heads > 65535) return fail(RCC_ERR_SHAPE, "n_heads must be in [1, 65535]");
+  if (q_tokens < 0 || kv_tokens < 0 || n_persist < 0 || n_local < 0)
+    return fail(RCC_ERR_SHAPE, "negative size");
+  if ((int64_t)n_persist + n_local > rcc::block_sparse_max_entries())
+    return fail(RCC_ERR_SHAPE, "n_persist + n_local must be at most %d",
+                rcc::block_sparse_max_entries());
+  if (kv_tokens / block_tokens > 32768)
+    return fail(RCC_ERR_SHAPE, "at most 32768 key blocks");
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(RCC_ERR_SHAPE, "scale must be positive and finite");
+  if (kv_tokens > cache_tokens)
+    return fail(RCC_ERR_RANGE, "kv_tokens %lld > cache_tokens %lld", (long long)kv_tokens,
+                (long long)cache_tokens);
+  // K/V loads use 32-bit byte offsets inside one batch entry's cache.
+  if (cache_tokens * n_heads * 256 > (int64_t)UINT32_MAX)
+    return fail(RCC_ERR_SHAPE, "a batch entry's cache must be smaller than 4 GiB");
+  const int64_t n_qb = (q_tokens + block_tokens - 1) / block_tokens;
+  if (q_tokens > kI32Max || n_qb * n_heads * batch > kI32Max)
+    return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
+  if (q_tokens == 0) return RCC_OK;
+  if (!q || !k_cache || !v_cache || !out || (n_persist && !persist) || (n_local && !local))
+    return fail(RCC_ERR_NULL, "a tensor or list pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      ((uintptr_t)persist & 3u) || ((uintptr_t)local & 3u))
+    return fail(RCC_ERR_ALIGN, "tensors must be 16-byte aligned, lists 4-byte");
+
+  rcc::SparseArgs a;
+  a.batch = batch;
+  a.n_heads = n_heads;
+  a.q_tokens = (int32_t)q_tokens;
+  a.kv_tokens = (int32_t)kv_tokens;
+  a.block_tokens = block_tokens;
+  a.n_qblocks = (int32_t)n_qb;
+  a.n_kblocks = (int32_t)(kv_tokens / block_tokens);
+  a.n_persist = n_persist;
+  a.n_local = n_local;
+  a.cache_tokens = cache_tokens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.persist = persist;
+  a.local = local;
+  a.out = out;
+  return from_hip(rcc::launch_block_sparse_attn(a, out_dtype, stream), "block_sparse_attn launch");
+}
+
 }  // extern "C"

@@ -102,4 +102,23 @@ hipError_t launch_chunk_causal_attn(const AttnArgs& a, rcc_dtype in, rcc_dtype o
 bool attn_d128_supported(const AttnArgs& a, rcc_dtype in);
 hipError_t launch_attn_d128(const AttnArgs& a, rcc_dtype out, hipStream_t s);
 
+// Block-sparse attention over a persistent + local block memory
+// (attn_sparse.hip; bf16, head_dim 128).
+struct SparseArgs {
+  int32_t batch, n_heads;
+  int32_t q_tokens, kv_tokens, block_tokens;  // block_tokens in {32, 64, 128, 256}
+  int32_t n_qblocks, n_kblocks;               // ceil(q_tokens / B), kv_tokens / B
+  int32_t n_persist, n_local;                 // list lengths
+  int64_t cache_tokens;
+  float scale_log2;                           // scale * log2(e)
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* persist;                     // [batch, n_heads, n_persist]
+  const int32_t* local;                       // [batch, n_heads, n_qblocks, n_local]
+  void* out;
+};
+int block_sparse_max_entries();               // n_persist + n_local limit
+hipError_t launch_block_sparse_attn(const SparseArgs& a, rcc_dtype out, hipStream_t s);
+
 }  // namespace rcc

@@ -184,6 +184,72 @@ WORKLOADS: Dict[str, Workload] = {
 SP_DEGREE = 8  # ranks the 480p_sp_shard workload is split over
 
 
+@dataclasses.dataclass(frozen=True)
+class SparseWorkload:
+    """Block-sparse attention over a persistent + local block memory.
+
+    The memory holds n_persist blocks, then the local window of n_window
+    blocks whose last q_blocks blocks are the query chunk's own (the chunk
+    was just written).  Each query block's local list holds its own block
+    (the diagonal) and top_k - 1 other window blocks drawn without
+    replacement; every query block also attends all persistent blocks.
+    """
+    name: str
+    n_heads: int
+    head_dim: int
+    block: int          # tokens per block, B_t * B_h * B_w
+    q_blocks: int       # query chunk
+    n_persist: int      # persistent blocks (sinks + kept history)
+    n_window: int       # local window blocks (includes the chunk)
+    top_k: int          # local blocks per query block
+    batch: int = 1
+
+    @property
+    def q_tokens(self) -> int:
+        return self.q_blocks * self.block
+
+    @property
+    def kv_tokens(self) -> int:
+        return (self.n_persist + self.n_window) * self.block
+
+    def flops(self) -> float:
+        keys = (self.n_persist + self.top_k) * self.block
+        return 4.0 * self.q_tokens * keys * self.head_dim * self.n_heads * self.batch
+
+
+def block_lists(w: SparseWorkload, seed: int):
+    """Seeded persistent and local block lists (int32) for workload w.
+
+    persist [batch, heads, n_persist] = blocks 0 .. n_persist-1 in a seeded
+    order; local [batch, heads, q_blocks, top_k] = the query block's own
+    block first, then distinct random window blocks.
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    persist = np.empty((w.batch, w.n_heads, w.n_persist), dtype=np.int32)
+    local = np.empty((w.batch, w.n_heads, w.q_blocks, w.top_k), dtype=np.int32)
+    lo = w.n_persist
+    own0 = w.n_persist + w.n_window - w.q_blocks
+    for b in range(w.batch):
+        for h in range(w.n_heads):
+            persist[b, h] = g.permutation(w.n_persist)
+            for i in range(w.q_blocks):
+                others = np.delete(np.arange(lo, lo + w.n_window), own0 + i - lo)
+                local[b, h, i, 0] = own0 + i
+                local[b, h, i, 1:] = g.choice(others, w.top_k - 1, replace=False)
+    return persist, local
+
+
+# Sparse Forcing's setting ([1,8,8] blocks of 64 tokens at 896x512: 32 x 56
+# patches, 28 blocks per latent frame): the query chunk is 3 frames (84
+# blocks), the local window 12 frames (336 blocks), the persistent memory
+# 6 frames' worth (168 blocks: 3 sink frames + 84 kept blocks); Top-K of
+# 25%, 12.5% and 6.25% of the local window.
+SPARSE_WORKLOADS: Dict[str, SparseWorkload] = {
+    name: SparseWorkload(name, 12, 128, 64, 84, 168, 336, k)
+    for name, k in (("sf512_top25", 84), ("sf512_top12.5", 42), ("sf512_top6.25", 21))
+}
+
+
 def seed_for(workload: str, start_frame: int, step: int, tensor: str) -> int:
     """Deterministic seed per (workload, chunk, step, tensor)."""
     base = {"tiny": 1, "480p_step": 20, "480p_rollout": 300,

@@ -223,3 +223,33 @@ def test_ring_positions_and_attention_host_checks():
     assert attn(g, r, head_dim=20) == rcc.RCC_ERR_SHAPE
     assert attn(g, r, out=FAKE + 8) == rcc.RCC_ERR_ALIGN
     assert attn(g, r, q_tokens=0) == rcc.RCC_OK
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dtype=rcc.RCC_F32), rcc.RCC_ERR_DTYPE),
+    (dict(out_dtype=5), rcc.RCC_ERR_DTYPE),
+    (dict(head_dim=64), rcc.RCC_ERR_SHAPE),
+    (dict(block=48), rcc.RCC_ERR_SHAPE),
+    (dict(block=512), rcc.RCC_ERR_SHAPE),
+    (dict(n_p=600, n_l=425), rcc.RCC_ERR_SHAPE),             # more than 1024 entries
+    (dict(kv=32768 * 32 + 32, cache=1 << 21, block=32), rcc.RCC_ERR_SHAPE),  # > 32768 blocks
+    (dict(kv=1025), rcc.RCC_ERR_RANGE),                      # beyond the cache
+    (dict(cache=1 << 22, nh=8), rcc.RCC_ERR_SHAPE),          # a batch entry's cache >= 4 GiB
+    (dict(scale=0.0), rcc.RCC_ERR_SHAPE),
+    (dict(n_l=-1), rcc.RCC_ERR_SHAPE),
+    (dict(persist=0), rcc.RCC_ERR_NULL),
+    (dict(local=FAKE + 2), rcc.RCC_ERR_ALIGN),
+    (dict(out=FAKE + 8), rcc.RCC_ERR_ALIGN),
+    (dict(q_tokens=0, q=0), rcc.RCC_OK),                     # nothing to do
+])
+def test_block_sparse_host_checks(kw, status):
+    a = dict(in_dtype=rcc.RCC_BF16, out_dtype=rcc.RCC_BF16, batch=1, nh=2, head_dim=128,
+             q_tokens=128, kv=1024, block=64, scale=0.1, q=FAKE, cache=1024, persist=FAKE,
+             n_p=3, local=FAKE, n_l=4, out=FAKE)
+    a.update(kw)
+    st = rcc.lib().rcc_block_sparse_attn(
+        a["in_dtype"], a["out_dtype"], a["batch"], a["nh"], a["head_dim"], a["q_tokens"], a["kv"],
+        a["block"], a["scale"], a["q"], FAKE, FAKE, a["cache"], a["persist"], a["n_p"],
+        a["local"], a["n_l"], a["out"], None)
+    assert st == status, rcc.lib().rcc_last_error()

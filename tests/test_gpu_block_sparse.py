@@ -1,0 +1,146 @@
+"""GPU parity: block_sparse_attn vs ``oracle.block_sparse``.
+
+Seeded bf16 N(0,1) q, k, v; block lists drawn with padding (-1), repeats and
+out-of-range entries mixed in, so the kernel's union has to drop them.
+Small cases are compared in full (ragged last query block, every block
+size); the Sparse Forcing-shaped workloads on sampled query blocks of every
+head.  Attention bar: max 2e-2 / mean 2e-3 (rel L2 1e-2).  Also: every block
+selected equals the dense kernel; empty unions give exact zeros; list order
+and padding leave the output bit-identical.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import rope_chunk_causal_amd as rcc
+from gpu_util import check_attn, say, to_dev, to_host_f64, torch
+from oracle import block_sparse as S
+from rope_chunk_causal_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _messy_lists(seed, B, nh, n_qb, n_kb, n_p, n_l):
+    g = np.random.Generator(np.random.PCG64(seed))
+    persist = g.integers(-1, n_kb + 3, size=(B, nh, n_p)).astype(np.int32)
+    local = g.integers(-2, n_kb + 3, size=(B, nh, n_qb, n_l)).astype(np.int32)
+    if n_l > 1:
+        local[..., -1] = local[..., 0]                   # a repeat in every list
+    return persist, local
+
+
+def _run(B, nh, n_q, kv, cap, blk, n_p, n_l, seed, out_dtype="bf16", lists=None):
+    t = torch()
+    D = 128
+    qb = synth.normal((B, n_q, nh, D), seed, "bf16")
+    kb = synth.normal((B, cap, nh, D), seed + 1, "bf16")
+    vb = synth.normal((B, cap, nh, D), seed + 2, "bf16")
+    n_qb = -(-n_q // blk)
+    persist, local = lists if lists is not None else _messy_lists(seed + 3, B, nh, n_qb, kv // blk,
+                                                                  n_p, n_l)
+    dq, dk, dv = to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16")
+    odt = t.bfloat16 if out_dtype == "bf16" else t.float32
+    out = t.full((B, n_q, nh, D), float("nan"), dtype=odt, device="cuda")
+    dp = t.from_numpy(persist).cuda() if persist.shape[-1] else None
+    dl = t.from_numpy(local).cuda() if local.shape[-1] else None
+    say("block_sparse", B, nh, n_q, kv, cap, blk, persist.shape, local.shape, out_dtype)
+    rcc.block_sparse_attn(dq, dk, dv, out, kv, blk, dp, dl, 1.0 / math.sqrt(D))
+    t.cuda.synchronize()
+    return out, (qb, kb, vb), (persist, local)
+
+
+@pytest.mark.parametrize("B,nh,n_q,kv,cap,blk,n_p,n_l,out_dtype", [
+    (1, 2, 150, 640, 700, 64, 2, 3, "bf16"),     # ragged last query block, spare cache rows
+    (2, 3, 64, 1024, 1024, 32, 4, 6, "bf16"),
+    (1, 2, 300, 1280, 1300, 128, 1, 4, "f32"),
+    (1, 1, 512, 2560, 2560, 256, 3, 2, "bf16"),
+    (1, 2, 128, 4096, 4096, 64, 0, 9, "bf16"),   # local lists only
+    (1, 2, 128, 4096, 4096, 64, 7, 0, "bf16"),   # persistent list only
+])
+def test_small_shapes_every_row(B, nh, n_q, kv, cap, blk, n_p, n_l, out_dtype):
+    out, (qb, kb, vb), (persist, local) = _run(B, nh, n_q, kv, cap, blk, n_p, n_l, 31, out_dtype)
+    ref = S.block_sparse_attention(synth.to_f64(qb, "bf16"), synth.to_f64(kb, "bf16"),
+                                   synth.to_f64(vb, "bf16"), kv, blk, persist, local,
+                                   1.0 / math.sqrt(128))
+    got = to_host_f64(out)
+    empty = ~np.abs(ref).any(axis=-1)
+    assert np.array_equal(got[empty], ref[empty])       # empty unions: exact zeros
+    check_attn(got, ref, f"sparse B{B} q{n_q} kv{kv} blk{blk}")
+
+
+def test_every_block_selected_matches_the_dense_kernel():
+    t = torch()
+    nh, n_q, kv, blk = 2, 256, 2048, 64
+    n_kb = kv // blk
+    persist = np.tile(np.arange(0, n_kb, 2, dtype=np.int32), (1, nh, 1))
+    local = np.tile(np.arange(1, n_kb, 2, dtype=np.int32), (1, nh, n_q // blk, 1))
+    out, (qb, kb, vb), _ = _run(1, nh, n_q, kv, kv, blk, 0, 0, 41, lists=(persist, local))
+    dq, dk, dv = to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16")
+    dense = t.empty_like(out)
+    rcc.chunk_causal_attn(dq, dk, dv, dense, kv - n_q, kv, n_q, 1.0 / math.sqrt(128))
+    t.cuda.synchronize()
+    check_attn(to_host_f64(out), to_host_f64(dense), "sparse vs dense kernel",
+               max_abs=4e-3, mean_abs=4e-4, rel_l2=2e-3)
+
+
+def test_empty_selection_gives_zeros():
+    t = torch()
+    persist = np.full((1, 2, 3), -1, dtype=np.int32)
+    local = np.array([[[[99, -1]], [[4, 5]]]], dtype=np.int32).reshape(1, 2, 1, 2)
+    out, _, _ = _run(1, 2, 64, 320, 320, 64, 0, 0, 51, lists=(persist, local))
+    assert bool((out[:, :, 0] == 0).all())              # head 0: nothing valid
+    assert bool(t.isfinite(out).all())
+
+
+def test_list_order_and_padding_do_not_change_bits():
+    t = torch()
+    B, nh, n_q, kv, blk = 1, 2, 192, 1536, 64
+    g = np.random.Generator(np.random.PCG64(61))
+    persist = g.choice(24, size=(B, nh, 4), replace=False).astype(np.int32)
+    local = np.stack([np.stack([g.choice(24, 5, replace=False) for _ in range(3)])
+                      for _ in range(nh)])[None].astype(np.int32)
+    a, _, _ = _run(B, nh, n_q, kv, kv, blk, 0, 0, 62, lists=(persist, local))
+    messy_p = np.concatenate([persist[..., ::-1], np.full((B, nh, 2), -1, np.int32)], axis=-1)
+    messy_l = np.concatenate([local[..., ::-1], persist[:, :, None, :2].repeat(3, axis=2),
+                              np.full((B, nh, 3, 1), 77, np.int32)], axis=-1)
+    b, _, _ = _run(B, nh, n_q, kv, kv, blk, 0, 0, 62, lists=(np.ascontiguousarray(messy_p),
+                                                              np.ascontiguousarray(messy_l)))
+    assert bool((a.view(t.int16) == b.view(t.int16)).all())
+
+
+@pytest.mark.parametrize("name", sorted(synth.SPARSE_WORKLOADS))
+def test_sparse_forcing_shapes_sampled(name):
+    w = synth.SPARSE_WORKLOADS[name]
+    persist, local = synth.block_lists(w, 7)
+    out, (qb, kb, vb), _ = _run(w.batch, w.n_heads, w.q_tokens, w.kv_tokens, w.kv_tokens, w.block,
+                                0, 0, 71, lists=(persist, local))
+    rng = np.random.default_rng(8)
+    blocks = np.unique(np.concatenate([rng.choice(w.q_blocks, 5, replace=False),
+                                       [0, w.q_blocks - 1]]))
+    rows = (blocks[:, None] * w.block + np.arange(w.block)[None, :]).reshape(-1)
+    ref = S.block_sparse_attention(synth.to_f64(qb, "bf16")[:, rows], synth.to_f64(kb, "bf16"),
+                                   synth.to_f64(vb, "bf16"), w.kv_tokens, w.block, persist,
+                                   local[:, :, blocks], 1.0 / math.sqrt(w.head_dim))
+    check_attn(to_host_f64(out[:, rows]), ref, name)
+
+
+def test_errors_reported_without_launch():
+    t = torch()
+    q = t.zeros((1, 64, 2, 128), dtype=t.bfloat16, device="cuda")
+    kc = t.zeros((1, 256, 2, 128), dtype=t.bfloat16, device="cuda")
+    out = t.full_like(q, 3.0)
+    lists = t.zeros((1, 2, 1, 2), dtype=t.int32, device="cuda")
+    for kw, status in ((dict(block_tokens=48), rcc.RCC_ERR_SHAPE),
+                       (dict(kv_tokens=257), rcc.RCC_ERR_RANGE)):
+        a = dict(kv_tokens=256, block_tokens=64)
+        a.update(kw)
+        with pytest.raises(rcc.RccError) as e:
+            rcc.block_sparse_attn(q, kc, kc, out, a["kv_tokens"], a["block_tokens"], None, None,
+                                  0.1)
+        assert e.value.status == status
+    with pytest.raises(rcc.RccError) as e:
+        rcc.block_sparse_attn(q.float(), kc.float(), kc.float(), out.float(), 256, 64, None,
+                              lists, 0.1)
+    assert e.value.status == rcc.RCC_ERR_DTYPE
+    assert bool((out == 3.0).all())
