@@ -183,6 +183,7 @@ def main():
     rollout = rollout_480p(rcc, synth, cfg, tables, randn, stream, dev)
     qkv = qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev)
     rolling = rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev)
+    sparse = block_sparse(rcc, synth, randn, stream, dev)
 
     traffic = read_traffic("chunk_causal_attn_480p_step")
     result = {
@@ -212,6 +213,7 @@ def main():
         "rollout_480p": rollout,
         "qkv_rope_append": qkv,
         "rolling_1min": rolling,
+        "block_sparse": sparse,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -445,6 +447,48 @@ def rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev):
                            "attn_tflops": round(f_flop / (sum(f_attn) * 1e-3) / 1e12, 1),
                            "last_attn_ms_per_step": round(f_attn[-1], 4),
                            "cache_rows": full_rows, "kv_bytes": full_rows * kv_bytes}}
+
+
+def block_sparse(rcc, synth, randn, stream, dev):
+    """Block-sparse attention on the Sparse Forcing-shaped memory (query
+    chunk of 84 blocks of 64 tokens, 168 persistent + 336 local-window blocks,
+    12 heads) at Top-K 25 / 12.5 / 6.25 % of the window, beside the dense
+    kernel over the whole memory (every key visible).  TFLOP/s counts the
+    selected query-key pairs only.  HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    out = {}
+    w0 = next(iter(synth.SPARSE_WORKLOADS.values()))
+    q = randn(1, w0.q_tokens, w0.n_heads, w0.head_dim)
+    k = randn(1, w0.kv_tokens, w0.n_heads, w0.head_dim)
+    v = randn(1, w0.kv_tokens, w0.n_heads, w0.head_dim)
+    o = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(w0.head_dim)
+
+    def dense(i):
+        rcc.chunk_causal_attn(q, k, v, o, w0.kv_tokens - w0.q_tokens, w0.kv_tokens, w0.q_tokens,
+                              scale, stream=stream)
+    for i in range(3):
+        dense(i)
+    d_ms = _time_events(dense, stream, 20)
+    d_flop = 4.0 * w0.q_tokens * w0.kv_tokens * w0.head_dim * w0.n_heads
+    for name, w in synth.SPARSE_WORKLOADS.items():
+        p, l = synth.block_lists(w, 7)
+        dp = torch.from_numpy(p).to(dev)
+        dl = torch.from_numpy(np.ascontiguousarray(l)).to(dev)
+
+        def run(i):
+            rcc.block_sparse_attn(q, k, v, o, w.kv_tokens, w.block, dp, dl, scale, stream=stream)
+        for i in range(3):
+            run(i)
+        ms = _time_events(run, stream, 20)
+        out[name] = {"top_k_blocks": w.top_k, "ms": round(ms, 4),
+                     "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1),
+                     "speedup_vs_dense": round(d_ms / ms, 3), "flop": w.flops()}
+    out["dense_full_memory"] = {"ms": round(d_ms, 4),
+                                "tflops": round(d_flop / (d_ms * 1e-3) / 1e12, 1),
+                                "q_tokens": w0.q_tokens, "kv_tokens": w0.kv_tokens}
+    return out
 
 
 def cpu_baseline(rows_per_head, wl, s, kv, scale):

@@ -8,7 +8,9 @@ chunk, 12 heads), rope_sp_b64 (585-token rank slice, 64 chunks batched),
 qkv_480p / qkv_sp_b64 (qkv_rope_append, model dim 1536 -> 3 x 12 x 128, on
 the same two token sets), ring_1min (one layer of a 1-minute rollout, 80
 chunks x 4 steps, RoPE + ring write then attention over a 21-frame rolling
-window), copy (a plain 1 GiB device-to-device copy: the
+window), sparse_sf512 (block_sparse_attn on the Sparse Forcing-shaped
+memory at Top-K 25, 12.5 and 6.25 %, then the dense kernel over the same
+memory), copy (a plain 1 GiB device-to-device copy: the
 reference for scaling HBM byte counters), all (every one of them: copy,
 then the others in the order listed).  Inputs are seeded
 N(0,1) bf16 on the device; nothing is checked here (the tests do that).
@@ -108,6 +110,23 @@ def ring_1min(reps: int, gen) -> None:
                 rcc.chunk_causal_attn_ring(g, ring, qo, kc, vc, out, 1 / math.sqrt(D))
 
 
+def sparse_sf512(reps: int, gen) -> None:
+    w0 = next(iter(synth.SPARSE_WORKLOADS.values()))
+    q = _randn(gen, 1, w0.q_tokens, w0.n_heads, w0.head_dim)
+    k = _randn(gen, 1, w0.kv_tokens, w0.n_heads, w0.head_dim)
+    v = _randn(gen, 1, w0.kv_tokens, w0.n_heads, w0.head_dim)
+    o = torch.empty_like(q)
+    scale = 1 / math.sqrt(w0.head_dim)
+    for w in synth.SPARSE_WORKLOADS.values():
+        p, l = synth.block_lists(w, 7)
+        dp, dl = torch.from_numpy(p).cuda(), torch.from_numpy(l).cuda()
+        for _ in range(reps):
+            rcc.block_sparse_attn(q, k, v, o, w.kv_tokens, w.block, dp, dl, scale)
+    for _ in range(reps):
+        rcc.chunk_causal_attn(q, k, v, o, w0.kv_tokens - w0.q_tokens, w0.kv_tokens, w0.q_tokens,
+                              scale)
+
+
 def copy(reps: int) -> None:
     a = torch.ones(COPY_BYTES // 2, device="cuda", dtype=torch.bfloat16)
     b = torch.empty_like(a)
@@ -118,14 +137,15 @@ def copy(reps: int) -> None:
 def main() -> None:
     p = argparse.ArgumentParser()
     p.add_argument("workload", choices=["attn_480p", "attn_720p", "rope_480p", "rope_sp_b64",
-                                        "qkv_480p", "qkv_sp_b64", "ring_1min", "copy", "all"])
+                                        "qkv_480p", "qkv_sp_b64", "ring_1min", "sparse_sf512",
+                                        "copy", "all"])
     p.add_argument("--reps", type=int, default=3)
     a = p.parse_args()
     rcc.lib()
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
     names = ["copy", "attn_480p", "attn_720p", "rope_480p", "rope_sp_b64", "qkv_480p",
-             "qkv_sp_b64"] \
+             "qkv_sp_b64", "sparse_sf512"] \
         if a.workload == "all" else [a.workload]
     for n in names:
         if n == "copy":
@@ -136,6 +156,8 @@ def main() -> None:
             qkv(n, a.reps, gen)
         elif n == "ring_1min":
             ring_1min(a.reps, gen)
+        elif n == "sparse_sf512":
+            sparse_sf512(a.reps, gen)
         else:
             rope(n, a.reps, gen)
         torch.cuda.synchronize()
