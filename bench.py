@@ -45,7 +45,7 @@ def parse():
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("attn.hip", "attn_d128.hip", "rcc_internal.h"):
+    for f in ("attn.hip", "attn_d128.hip", "attn_tile.h", "rcc_internal.h"):
         with open(os.path.join(ROOT, "rope_chunk_causal_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
