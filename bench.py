@@ -6,7 +6,11 @@ rope3d_apply_append on the 4680-token chunk at global frames 6..8 (12 heads,
 head_dim 128, bf16) writing rotated K and V into the cache, then
 chunk_causal_attn of the chunk's 4680 queries over the 14040 cached keys
 (frames 0..8).  The cos/sin tables are built once per process before timing,
-as the method prescribes (precomputed, not per call).
+as the method prescribes (precomputed, not per call).  Before the W warm-up
+steps the step runs untimed for PREWARM_S seconds: the board's power
+management takes tens of milliseconds to settle its clocks after idle, and a
+timed region that starts earlier measures that ramp rather than the kernels
+(the first 20 steps after idle run ~20% slower than the steady state).
 
 Prints ONE JSON line.  `value` is the step's attention TFLOP/s over the whole
 step time (RoPE included); the roofline object is for the dominant kernel
@@ -30,13 +34,14 @@ METRIC = "chunk-causal attn TFLOP/s + ms/chunk (Wan-1.3B 480P); RoPE kernel GB/s
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 N_SETS = 6  # rotating input sets: > 256 MB of traffic between reuses of one set
+PREWARM_S = 0.25  # untimed steps before the warm-up, so the clocks have settled
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4680,
                    help="query rows per head in the oracle's timed sample")
@@ -119,17 +124,26 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        s = stream
         st = sets[i % N_SETS]
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].record(s)
         rcc.rope3d_apply_append(cfg, tables, grid, st["q"], st["k"], st["v"], st["q_out"],
-                                st["kc"], st["vc"], stream=stream)
+                                st["kc"], st["vc"], stream=s)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record(s)
         rcc.chunk_causal_attn(st["q_out"], st["kc"], st["vc"], st["out"], q_pos, kv, L, scale,
-                              stream=stream)
+                              stream=s)
         if ev is not None:
-            ev[2].record(stream)
+            ev[2].record(s)
+
+    prewarm = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PREWARM_S:
+        for _ in range(10):
+            step(prewarm)
+            prewarm += 1
+        torch.cuda.synchronize()
 
     for i in range(args.warmup):
         step(i)
@@ -203,6 +217,7 @@ def main():
                    "rope_bands": [r.d_t, r.d_h, r.d_w], "grid": [wl.frames, wl.height, wl.width],
                    "start_frame": s, "q_tokens": L, "kv_tokens": kv, "batch": 1},
         "ms_per_chunk": round(ms_per_step, 4),
+        "prewarm_steps": prewarm,
         "attn_ms": round(attn_ms, 4),
         "attn_tflops": round(attn_tflops, 2),
         "rope_ms": round(rope_ms, 4),
