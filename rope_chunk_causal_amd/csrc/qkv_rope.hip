@@ -15,20 +15,24 @@
 // rounding of q and k before the rotation, unlike a projection followed by a
 // separate RoPE kernel).
 //
-// * Workgroup = 8 waves = 256 features x 256 tokens; wave (wf, wt) owns
-//   128 features x 64 tokens (4 x 2 accumulator blocks, 128 VGPRs): per
-//   16-deep k-step, 6 fragment reads feed 8 MFMAs.
-// * W and x stream through a ring of four LDS stages of 32 K-columns each
-//   (W tile at +0, x tile at +16 KB; 128 KB) with global_load_lds_dwordx4;
-//   tile t is computed while t+1 and t+2 are in flight and t+3 starts into the
-//   stage t-1 used.  Loads are branch-free (row and k indices clamped), so
-//   the compiler tracks which stage each load writes.
+// * Workgroup = 8 waves = 256 features x BT tokens (BT = 256 or 384); wave
+//   (wf, wt) owns 128 features x BT/4 tokens (4 x TB accumulator blocks,
+//   TB = BT/128): per 16-deep k-step, 4 + TB fragment reads feed 4 TB MFMAs.
+//   The host picks BT per call so that the grid fills the 256 CUs in the
+//   fewest rounds: a 4680-token chunk is 13 x 18 = 234 workgroups of 384
+//   tokens (one round) against 19 x 18 = 342 of 256 (two rounds).
+// * W and x stream through a ring of LDS stages of 32 K-columns each (W tile
+//   at +0, x tile after it) with global_load_lds_dwordx4: with S stages, tile
+//   t is computed while the next S - 2 are in flight and tile t + S - 1
+//   starts into the stage t - 1 used.  Loads are branch-free (row and k
+//   indices clamped), so the compiler tracks which stage each load writes.
 // * Both operands are K-contiguous rows (64 B per row per stage) with the
 //   16-byte chunk swizzle c ^ ((row / 4) % 4), which makes the ds_read_b128
 //   fragment reads bank-conflict free.
-// * Epilogue: bias and rotation in registers, bf16 results staged through
-//   the (then free) LDS ring so that 16 lanes write each token's 256 B of a
-//   wave's 128 features with one 16-byte store each.
+// * Epilogue, one 32-token block at a time: bias and rotation in registers,
+//   bf16 results staged through the (then free) LDS ring so that 16 lanes
+//   write each token's 256 B of a wave's 128 features with one 16-byte store
+//   each.
 #include "rcc_internal.h"
 
 namespace rcc {
@@ -38,11 +42,9 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBF = 256;                 // features per workgroup
-constexpr int kBT = 256;                 // tokens per workgroup
 constexpr int kBK = 32;                  // K columns per stage
 constexpr int kRowBytes = kBK * 2;       // 64 B per row per stage
-constexpr int kTileBytes = 256 * kRowBytes;  // 16 KB per operand per stage
-constexpr int kStages = 4;
+constexpr int kWTile = kBF * kRowBytes;  // 16 KB of W per stage
 constexpr int kXcds = 8;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -51,36 +53,52 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-struct StagePtrs {
-  char *w0, *x0, *w1, *x1, *w2, *x2, *w3, *x3;
+template <int BT>
+struct Tile {
+  static constexpr int kTB = BT / 128;            // 32-token blocks per wave
+  static constexpr int kXTile = BT * kRowBytes;   // x bytes per stage
+  static constexpr int kStage = kWTile + kXTile;  // 32 or 40 KB
+  static constexpr int kStages = BT == 256 ? 4 : 3;
+  static constexpr int kXInstr = BT / 128;        // x DMA instructions per wave per stage
+  static constexpr int kInstr = 2 + kXInstr;      // all DMA instructions per wave per stage
 };
 
-// Wave w loads rows 32 w .. 32 w + 31 of the W tile and of the x tile of
-// K-columns [k0, k0 + 32), two instructions of 16 rows each: lane l -> row
-// 32 w + 16 i + l/4, LDS chunk slot l%4, global chunk (l%4) ^ ((row / 4) % 4).
-// Rows past the matrix re-read its last row (their outputs are not stored);
-// k0 past the end re-reads the last K-columns into a stage no step reads
-// again.
+// Wave w loads W rows 32 w .. 32 w + 31 (two instructions of 16 rows) and x
+// rows (BT/8) w .. (BT/8) (w + 1) - 1 (BT/128 instructions) of K-columns
+// [k0, k0 + 32): lane l -> row base + 16 i + l/4, LDS chunk slot l%4, global
+// chunk (l%4) ^ ((row / 4) % 4).  Rows past the matrix re-read its last row
+// (their outputs are not stored); k0 past the end re-reads the last
+// K-columns into a stage no step reads again.
+template <int BT>
 __device__ __forceinline__ void issue_stage(const __bf16* w, const __bf16* x, int f0, int t0,
                                             int n_feat, int n_tok, int K, int k0, char* ws,
-                                            char* xs, int wave, int lane) {
+                                            int wave, int lane) {
+  using T = Tile<BT>;
   k0 = __builtin_amdgcn_readfirstlane(min(k0, K - kBK));
+  char* xs = ws + kWTile;
+  const uint32_t row_bytes = (uint32_t)(K * 2);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 32 * wave + 16 * i + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    const uint32_t kb = (uint32_t)(k0 * 2 + c * 16);
     const uint32_t wrow = (uint32_t)min(f0 + r, n_feat - 1);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const char*>(w) + (wrow * row_bytes + (uint32_t)(k0 * 2 + c * 16)),
+        (lds_void*)(ws + (2 * wave + i) * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < T::kXInstr; ++i) {
+    const int r = 16 * (T::kXInstr * wave + i) + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     const uint32_t xrow = (uint32_t)min(t0 + r, n_tok - 1);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(w) + (wrow * (uint32_t)(K * 2) + kb),
-                                     (lds_void*)(ws + (2 * wave + i) * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(x) + (xrow * (uint32_t)(K * 2) + kb),
-                                     (lds_void*)(xs + (2 * wave + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const char*>(x) + (xrow * row_bytes + (uint32_t)(k0 * 2 + c * 16)),
+        (lds_void*)(xs + (T::kXInstr * wave + i) * 1024), 16, 0, 0);
   }
 }
 
-// At most n of this wave's loads in flight (4 per stage), then a barrier
-// without a memory fence (a fence would also wait for the later stages).
+// At most n of this wave's loads in flight, then a barrier without a memory
+// fence (a fence would also wait for the later stages).
 template <int n>
 __device__ __forceinline__ void stage_ready() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
@@ -89,20 +107,27 @@ __device__ __forceinline__ void stage_ready() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+template <int BT>
 __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_ft) {
-  __shared__ __align__(1024) char sS0[2 * kTileBytes];
-  __shared__ __align__(1024) char sS1[2 * kTileBytes];
-  __shared__ __align__(1024) char sS2[2 * kTileBytes];
-  __shared__ __align__(1024) char sS3[2 * kTileBytes];
-  const StagePtrs st{sS0, sS0 + kTileBytes, sS1, sS1 + kTileBytes,
-                     sS2, sS2 + kTileBytes, sS3, sS3 + kTileBytes};
+  using T = Tile<BT>;
+  constexpr int S = T::kStages;
+  constexpr int TB = T::kTB;
+  // One object per stage, so the compiler does not order a stage's LDS reads
+  // after another stage's DMA writes; each lies below 64 KB.
+  __shared__ __align__(1024) char sS0[T::kStage];
+  __shared__ __align__(1024) char sS1[T::kStage];
+  __shared__ __align__(1024) char sS2[T::kStage];
+  __shared__ __align__(1024) char sS3[S > 3 ? T::kStage : 16];
+  auto stage = [&](int u) -> char* {
+    return u == 0 ? sS0 : u == 1 ? sS1 : u == 2 ? sS2 : sS3;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int wf = wave >> 2;   // 128-feature half
-  const int wt = wave & 3;    // 64-token quarter
+  const int wt = wave & 3;    // token quarter
 
   // XCD-major numbering: an XCD's workgroups take consecutive ids, which
   // walk the feature tiles of one token tile (sharing its x rows in L2).
@@ -112,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   const int xcd = blockIdx.x % kXcds;
   const int id = xcd * per - (rem && xcd > rem ? xcd - rem : 0) + blockIdx.x / kXcds;
   const int f0 = (id % n_ft) * kBF;
-  const int t0 = (id / n_ft) * kBT;
+  const int t0 = (id / n_ft) * BT;
 
   const int K = a.model_dim;
   const int hd = a.n_heads * a.head_dim;
@@ -122,83 +147,87 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   const __bf16* x = reinterpret_cast<const __bf16*>(a.x);
   const int steps = K / kBK;
 
-  issue_stage(w, x, f0, t0, n_feat, n_tok, K, 0, st.w0, st.x0, wave, lane);
-  issue_stage(w, x, f0, t0, n_feat, n_tok, K, kBK, st.w1, st.x1, wave, lane);
-  issue_stage(w, x, f0, t0, n_feat, n_tok, K, 2 * kBK, st.w2, st.x2, wave, lane);
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u)
+    issue_stage<BT>(w, x, f0, t0, n_feat, n_tok, K, u * kBK, stage(u), wave, lane);
 
   // chunk 2 kk + g of row r sits in slot (2 kk + g) ^ ((r / 4) % 4)
   const int sw0 = (g ^ ((l32 >> 2) & 3)) << 4;
   const int sw1 = ((2 + g) ^ ((l32 >> 2) & 3)) << 4;
   const int aoff0 = (wf * 128 + l32) * kRowBytes + sw0, aoff1 = aoff0 - sw0 + sw1;
-  const int boff0 = (wt * 64 + l32) * kRowBytes + sw0, boff1 = boff0 - sw0 + sw1;
+  const int boff0 = kWTile + (wt * 32 * TB + l32) * kRowBytes + sw0, boff1 = boff0 - sw0 + sw1;
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][TB];
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = f32x16{};
+    for (int tb = 0; tb < TB; ++tb) acc[fb][tb] = f32x16{};
 
-  auto step = [&](int t, const char* ws, const char* xs, char* wn, char* xn) {
-    stage_ready<8>();
-    issue_stage(w, x, f0, t0, n_feat, n_tok, K, (t + 3) * kBK, wn, xn, wave, lane);
+  auto step = [&](int t, int u) {
+    stage_ready<(S - 2) * T::kInstr>();
+    issue_stage<BT>(w, x, f0, t0, n_feat, n_tok, K, (t + S - 1) * kBK, stage((u + S - 1) % S),
+                    wave, lane);
+    const char* sp = stage(u);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int ao = kk ? aoff1 : aoff0, bo = kk ? boff1 : boff0;
-      bf16x8 af[4], bfr[2];
+      bf16x8 af[4], bfr[TB];
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) af[fb] = *reinterpret_cast<const bf16x8*>(ws + ao + fb * 32 * kRowBytes);
+      for (int fb = 0; fb < 4; ++fb) af[fb] = *reinterpret_cast<const bf16x8*>(sp + ao + fb * 32 * kRowBytes);
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const bf16x8*>(xs + bo + tb * 32 * kRowBytes);
+      for (int tb = 0; tb < TB; ++tb) bfr[tb] = *reinterpret_cast<const bf16x8*>(sp + bo + tb * 32 * kRowBytes);
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma32(af[fb], bfr[tb], acc[fb][tb]);
+        for (int tb = 0; tb < TB; ++tb) acc[fb][tb] = mfma32(af[fb], bfr[tb], acc[fb][tb]);
     }
   };
   int t = 0;
-  for (; t + kStages <= steps; t += kStages) {
-    step(t, st.w0, st.x0, st.w3, st.x3);
-    step(t + 1, st.w1, st.x1, st.w0, st.x0);
-    step(t + 2, st.w2, st.x2, st.w1, st.x1);
-    step(t + 3, st.w3, st.x3, st.w2, st.x2);
+  for (; t + S <= steps; t += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) step(t + u, u);
   }
-  if (t < steps) step(t, st.w0, st.x0, st.w3, st.x3);
-  if (t + 1 < steps) step(t + 1, st.w1, st.x1, st.w0, st.x0);
-  if (t + 2 < steps) step(t + 2, st.w2, st.x2, st.w1, st.x1);
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u)
+    if (t + u < steps) step(t + u, u);
   // Every load has landed and every wave is done with the stages: they now
   // hold the output tiles.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Epilogue 1 (registers -> LDS): bias and the rotation of q and k in fp32,
-  // rounded to bf16, into this wave's 64 x 128 output tile (token-major,
-  // 256 B per token; 16-byte chunk c of token t at slot c ^ (t % 16)).
-  char* tile = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1 : (wave >> 1) == 2 ? sS2 : sS3;
-  tile += (wave & 1) * (kTileBytes);
+  // Epilogue, per 32-token block of the wave: (1) registers -> LDS: bias
+  // and the rotation of q and k in fp32, rounded to bf16, into this wave's
+  // 32 x 128 staging tile (token-major, 256 B per token; 16-byte chunk c of
+  // token t at slot c ^ (t % 16)); (2) LDS -> global: 16 lanes write one
+  // token's 256 B, 4 tokens per instruction.  A wave reads back only what it
+  // wrote, and its LDS operations complete in order: no barrier.
+  char* tile = stage(wave >> 2) + (wave & 3) * 8192;
   const float2* tab = reinterpret_cast<const float2*>(a.tables);
-  TokenPos pos[2];
+  const int c = lane & 15;
+  const int fc = f0 + wf * 128 + c * 8;
+  const int which_c = fc / hd;
+  const int fr = fc - which_c * hd;
+  const int head = fr / a.head_dim;
+  const int dcol = head * a.head_dim + (fr - head * a.head_dim);
+  __bf16* obase = reinterpret_cast<__bf16*>(which_c == 0 ? a.q_out : which_c == 1 ? a.k_cache : a.v_cache);
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int m = min(t0 + wt * 64 + tb * 32 + l32, n_tok - 1);
-    pos[tb] = token_position(a.grid, m - (m / a.n_tokens) * a.n_tokens);
-  }
-  // Per 32-feature block, every global load it needs (bias, and cos/sin of
-  // its 8 rotary pairs for both tokens of the lane) is issued before any is
-  // used: one wait per block instead of one memory round trip per pair.
+  for (int tb = 0; tb < TB; ++tb) {
+    const int m = min(t0 + wt * 32 * TB + tb * 32 + l32, n_tok - 1);
+    const TokenPos pos = token_position(a.grid, m - (m / a.n_tokens) * a.n_tokens);
+    // Per 32-feature block, every global load it needs (bias, and cos/sin of
+    // its 8 rotary pairs for the lane's token) is issued before any is used.
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
-    const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
-    if (f >= n_feat) continue;
-    const int which = f / hd;
-    const int d0 = (f - which * hd) % a.head_dim;
-    f32x4 bias[4];
+    for (int fb = 0; fb < 4; ++fb) {
+      const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
+      if (f >= n_feat) continue;
+      const int which = f / hd;
+      const int d0 = (f - which * hd) % a.head_dim;
+      f32x4 bias[4];
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4)
-      bias[j4] = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + f + j4 * 8 + g * 4) : f32x4{};
-    float2 cs[2][4][2];
-    if (which < 2) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int j4 = 0; j4 < 4; ++j4)
+        bias[j4] = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + f + j4 * 8 + g * 4) : f32x4{};
+      float2 cs[4][2];
+      if (which < 2) {
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
@@ -206,18 +235,15 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
             const int pr = ((d0 + j4 * 8 + g * 4) >> 1) + e;  // rotary pair inside the head
             const float2* src;
             if (pr < a.pt) {
-              src = tab + (int64_t)pos[tb].t * a.pt + pr;
+              src = tab + (int64_t)pos.t * a.pt + pr;
             } else if (pr < a.pt + a.ph) {
-              src = tab + a.off_h + (int64_t)pos[tb].h * a.ph + (pr - a.pt);
+              src = tab + a.off_h + (int64_t)pos.h * a.ph + (pr - a.pt);
             } else {
-              src = tab + a.off_w + (int64_t)pos[tb].w * a.pw + (pr - a.pt - a.ph);
+              src = tab + a.off_w + (int64_t)pos.w * a.pw + (pr - a.pt - a.ph);
             }
-            cs[tb][j4][e] = *src;
+            cs[j4][e] = *src;
           }
-    }
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int tl = tb * 32 + l32;  // token within the wave tile
+      }
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         float y[4];
@@ -226,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
         if (which < 2) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float2 c2 = cs[tb][j4][e];
+            const float2 c2 = cs[j4][e];
             const float x0 = y[2 * e], x1 = y[2 * e + 1];
             y[2 * e] = x0 * c2.x - x1 * c2.y;
             y[2 * e + 1] = x0 * c2.y + x1 * c2.x;
@@ -237,40 +263,39 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
         v[1] = (__bf16)y[1];
         v[2] = (__bf16)y[2];
         v[3] = (__bf16)y[3];
-        const int c = fb * 4 + j4;  // 16-byte chunk of the 128 features
-        *reinterpret_cast<bf16x4*>(tile + tl * 256 + ((c ^ (tl & 15)) << 4) + g * 8) = v;
+        const int cc = fb * 4 + j4;  // 16-byte chunk of the 128 features
+        *reinterpret_cast<bf16x4*>(tile + l32 * 256 + ((cc ^ (l32 & 15)) << 4) + g * 8) = v;
       }
     }
-  }
-
-  // Epilogue 2 (LDS -> global): 16 lanes write one token's 256 B, 4 tokens
-  // per instruction.  Chunk c of the wave's features is one 8-feature run of
-  // one head of q, k or v.
-  const int c = lane & 15;
-  const int fc = f0 + wf * 128 + c * 8;
-  if (fc < n_feat) {
-    const int which = fc / hd;
-    const int fr = fc - which * hd;
-    const int head = fr / a.head_dim;
-    const int dcol = head * a.head_dim + (fr - head * a.head_dim);
-    __bf16* base = reinterpret_cast<__bf16*>(which == 0 ? a.q_out : which == 1 ? a.k_cache : a.v_cache);
+    // Chunk c of the wave's features is one 8-feature run of one head of q,
+    // k or v.
+    if (fc < n_feat) {
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int tl = it * 4 + (lane >> 4);
-      const int m = t0 + wt * 64 + tl;
-      if (m >= n_tok) break;
-      const int b = m / a.n_tokens;
-      const int i = m - b * a.n_tokens;
-      int64_t row;
-      if (which == 0) {
-        row = (int64_t)b * a.n_tokens + i;
-      } else {
-        row = (int64_t)b * a.cache_tokens + token_position(a.grid, i).row;
+      for (int it = 0; it < 8; ++it) {
+        const int tl = it * 4 + (lane >> 4);
+        const int mm = t0 + wt * 32 * TB + tb * 32 + tl;
+        if (mm >= n_tok) break;
+        const int b = mm / a.n_tokens;
+        const int i = mm - b * a.n_tokens;
+        int64_t row;
+        if (which_c == 0) {
+          row = (int64_t)b * a.n_tokens + i;
+        } else {
+          row = (int64_t)b * a.cache_tokens + token_position(a.grid, i).row;
+        }
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(tile + tl * 256 + ((c ^ (tl & 15)) << 4));
+        *reinterpret_cast<bf16x8*>(obase + row * hd + dcol) = v;
       }
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(tile + tl * 256 + ((c ^ (tl & 15)) << 4));
-      *reinterpret_cast<bf16x8*>(base + row * hd + dcol) = v;
     }
   }
+}
+
+template <int BT>
+hipError_t launch_bt(const QkvArgs& a, int n_ft, int64_t n_tok, hipStream_t s) {
+  const int64_t n_tt = (n_tok + BT - 1) / BT;
+  hipLaunchKernelGGL(qkv_rope_kernel<BT>, dim3((uint32_t)(n_ft * n_tt)), dim3(kThreads), 0, s, a,
+                     n_ft);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -279,9 +304,14 @@ hipError_t launch_qkv_rope_append(const QkvArgs& a, hipStream_t s) {
   const int n_feat = 3 * a.n_heads * a.head_dim;
   const int64_t n_tok = (int64_t)a.batch * a.n_tokens;
   const int n_ft = (n_feat + kBF - 1) / kBF;
-  const int64_t n_tt = (n_tok + kBT - 1) / kBT;
-  hipLaunchKernelGGL(qkv_rope_kernel, dim3((uint32_t)(n_ft * n_tt)), dim3(kThreads), 0, s, a, n_ft);
-  return hipGetLastError();
+  // Token tile that fills the CUs in the fewest rounds, counting a round of
+  // 384-token tiles as 1.5 rounds of 256-token ones.
+  constexpr int64_t kCUs = 256;
+  auto cost = [&](int64_t bt) {
+    const int64_t tiles = n_ft * ((n_tok + bt - 1) / bt);
+    return ((tiles + kCUs - 1) / kCUs) * bt;
+  };
+  return cost(384) < cost(256) ? launch_bt<384>(a, n_ft, n_tok, s) : launch_bt<256>(a, n_ft, n_tok, s);
 }
 
 }  // namespace rcc
