@@ -198,6 +198,7 @@ def main():
     qkv = qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev)
     rolling = rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev)
     sparse = block_sparse(rcc, synth, randn, stream, dev)
+    attn720 = attn_720p(rcc, synth, randn, stream, dev)
 
     traffic = read_traffic("chunk_causal_attn_480p_step")
     result = {
@@ -229,6 +230,7 @@ def main():
         "qkv_rope_append": qkv,
         "rolling_1min": rolling,
         "block_sparse": sparse,
+        "attn_720p": attn720,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -462,6 +464,33 @@ def rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev):
                            "attn_tflops": round(f_flop / (sum(f_attn) * 1e-3) / 1e12, 1),
                            "last_attn_ms_per_step": round(f_attn[-1], 4),
                            "cache_rows": full_rows, "kv_bytes": full_rows * kv_bytes}}
+
+
+def attn_720p(rcc, synth, randn, stream, dev):
+    """chunk_causal_attn on the Wan-14B-shaped 720P step: 10800 queries (frames
+    18..20) over 75600 keys, 40 heads; 2 untimed launches, then 10 timed with
+    HIP events on the launch stream."""
+    import torch
+    wl = synth.WORKLOADS["720p_step"]
+    s = wl.start_frames[0]
+    nh, D, L, hw = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.hw
+    kv = (s + wl.frames) * hw
+    q = randn(1, L, nh, D)
+    k = randn(1, kv, nh, D)
+    v = randn(1, kv, nh, D)
+    o = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(D)
+
+    def run(i):
+        rcc.chunk_causal_attn(q, k, v, o, s * hw, kv, L, scale, stream=stream)
+    for i in range(2):
+        run(i)
+    ms = _time_events(run, stream, 10)
+    flop = wl.attn_flops(s)
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "q_tokens": L,
+            "kv_tokens": kv, "heads": nh, "frac_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def block_sparse(rcc, synth, randn, stream, dev):

@@ -72,6 +72,15 @@ def test_small_shapes_every_token(B, n, nh, dims, K, F, H, W, s, off, bias):
     _run(B, n, nh, dims, K, F, H, W, s, off, (16, 16, 16), bias, seed=11)
 
 
+@pytest.mark.parametrize("n,nh,F,H,W", [
+    (3700, 12, 3, 30, 52),   # 18 feature tiles: 384-token tiles fill the CUs in one round
+    (9000, 5, 6, 30, 52),    # 1920 features: a ragged last feature tile
+])
+def test_384_token_tiles_every_token(n, nh, F, H, W):
+    """Shapes the host runs with 384-token tiles, compared on every token."""
+    _run(1, n, nh, (44, 42, 42), nh * 128, F, H, W, 2, 0, (16, 32, 64), True, 61)
+
+
 def test_480p_chunk_sampled_tokens():
     wl = synth.WORKLOADS["480p_step"]
     r = wl.rope
