@@ -314,9 +314,10 @@ RCC_API rcc_status rcc_chunk_causal_attn_ring(
  * repeated entries count once and entries outside [0, kv_tokens / B)
  * are ignored (-1 pads a list).  out = softmax(scale * q k^T) v over the
  * union's keys, fp32 softmax and accumulation, bf16 matrix-core operands;
- * a query block with an empty union gets zeros.  Keys are visited in
- * ascending block order whatever the lists' order, so the result does not
- * depend on it.
+ * a query block with an empty union gets zeros.  The order in which keys
+ * are visited depends only on the two sets (persistent blocks ascending,
+ * then the other local blocks ascending), never on the lists' order or
+ * padding, so neither changes a bit of the result.
  * Errors: NULL (a tensor, or a list whose length is non-zero); DTYPE
  * (in_dtype not bf16, unknown out_dtype); SHAPE (head_dim != 128,
  * block_tokens not 32, 64, 128 or 256, batch/n_heads non-positive,
