@@ -217,17 +217,31 @@ RCC_API rcc_status rcc_qkv_rope_append(
  * and the last window_frames frames ending at s+F-1, and these occupy
  * exactly ring rows [0, min(s+F, sink+window) * H*W): the visible memory is
  * always a prefix of the ring, so attention over it needs no gather.
+ *
+ * block_h, block_w > 0 store each frame block-contiguously ([SF] §3.3
+ * blockify, blocks one frame deep): the frame's (H/block_h) x (W/block_w)
+ * blocks in row-major order, each block's block_h x block_w tokens in
+ * row-major order, so token (h, w) is row slot(t) * H*W + b * block_h *
+ * block_w + (h % block_h) * block_w + w % block_w with b = (h / block_h) *
+ * (W / block_w) + w / block_w.  Block j of the held memory is then rows
+ * [j * block_h * block_w, (j+1) * block_h * block_w): the key blocks of
+ * rcc_block_sparse_attn with block_tokens = block_h * block_w.  Both 0
+ * (the default) keep the frame row-major.  A window that never wraps
+ * (window_frames >= every frame written) gives a blockified plain cache.
  */
 typedef struct {
   int32_t sink_frames;
   int32_t window_frames;
+  int32_t block_h;
+  int32_t block_w;
 } rcc_ring;
 
 /*
  * Ring rows the chunk described by `grid` attends once it is written:
  * min(s + F, sink + window) * H*W.  Host-only.  Returns -1 if grid or ring
  * is NULL or invalid (non-positive grid, s < 0, sink < 0,
- * window < F, or (sink + window) * H*W >= 2^31).
+ * window < F, (sink + window) * H*W >= 2^31, or block dims that are
+ * negative, only one of them zero, or not dividing H and W).
  */
 RCC_API int64_t rcc_ring_held_tokens(const rcc_grid* grid, const rcc_ring* ring);
 
@@ -235,7 +249,7 @@ RCC_API int64_t rcc_ring_held_tokens(const rcc_grid* grid, const rcc_ring* ring)
  * ring_positions — rcc_rope3d_positions with the ring row in column 3:
  * int32 [n_tokens][4] = {t_global, h, w, ring_row}.  A check/debug export.
  * Errors: as rcc_rope3d_positions, plus NULL ring and SHAPE (sink < 0,
- * window < F, (sink + window) * H*W >= 2^31).
+ * window < F, (sink + window) * H*W >= 2^31, invalid block dims).
  */
 RCC_API rcc_status rcc_ring_positions(const rcc_grid* grid, const rcc_ring* ring,
                                       int64_t n_tokens, int32_t* thw_dev, hipStream_t stream);
@@ -249,7 +263,7 @@ RCC_API rcc_status rcc_ring_positions(const rcc_grid* grid, const rcc_ring* ring
  * cache_tokens >= (sink + window) * H*W.
  * Errors: as rcc_rope3d_apply_append, with the RANGE rule on cache rows
  * replaced by cache_tokens < (sink + window) * H*W; NULL ring; SHAPE
- * (sink < 0, window < F, ring of 2^31 rows or more).
+ * (sink < 0, window < F, ring of 2^31 rows or more, invalid block dims).
  */
 RCC_API rcc_status rcc_rope3d_apply_append_ring(
     const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,

@@ -26,6 +26,11 @@ the readings taken here are:
 * Storage is a ring: frame t lives in frame slot t if t < sink, else in
   slot sink + (t - sink) mod window; token (h, w) of the frame is row
   slot * H*W + h*W + w of a cache of (sink + window) * H*W rows.
+* Optionally the tokens of a frame are stored block-contiguously ([SF]
+  §3.3 blockify, with blocks of (1, B_h, B_w): one frame deep): the
+  frame's (H/B_h) x (W/B_w) blocks in row-major order, each block's B_h x B_w
+  tokens in row-major order, so block j of a frame is rows
+  [j B_h B_w, (j+1) B_h B_w) of its slot.  B_h and B_w divide H and W.
 """
 from __future__ import annotations
 
@@ -61,22 +66,38 @@ def held_frames(frames: int, start_frame: int, sink: int, window: int) -> np.nda
                            np.arange(lo, end, dtype=np.int64)])
 
 
+def frame_row(h, w, height: int, width: int, block_h: int = 0, block_w: int = 0):
+    """Row of token (h, w) inside its frame slot: h*W + w, or, blockified,
+    (block index, row-major over the frame's blocks) * B_h B_w + (row-major
+    index inside the block)."""
+    h = np.asarray(h, dtype=np.int64)
+    w = np.asarray(w, dtype=np.int64)
+    if not block_h and not block_w:
+        return h * width + w
+    if block_h <= 0 or block_w <= 0 or height % block_h or width % block_w:
+        raise ValueError("block dims must be positive and divide the frame")
+    block = (h // block_h) * (width // block_w) + w // block_w
+    return block * (block_h * block_w) + (h % block_h) * block_w + w % block_w
+
+
 def positions(frames: int, height: int, width: int, start_frame: int, token_offset: int,
-              n_tokens: int, sink: int, window: int) -> np.ndarray:
+              n_tokens: int, sink: int, window: int, block_h: int = 0,
+              block_w: int = 0) -> np.ndarray:
     """(t_global, h, w, ring_row) of tokens token_offset .. +n_tokens-1.
 
     t, h, w are those of ``rope3d.positions`` ([YL] §3.3.3: global time index
     from the start frame and the slice offset); the row is the token's row in
-    the ring: frame_slot(t) * H*W + h*W + w.
+    the ring: frame_slot(t) * H*W + frame_row(h, w).
     """
     _check(frames, sink, window)
     pos = rope3d.positions(frames, height, width, start_frame, token_offset, n_tokens).copy()
-    pos[:, 3] = frame_slot(pos[:, 0], sink, window) * (height * width) + pos[:, 1] * width + pos[:, 2]
+    pos[:, 3] = (frame_slot(pos[:, 0], sink, window) * (height * width)
+                 + frame_row(pos[:, 1], pos[:, 2], height, width, block_h, block_w))
     return pos
 
 
 def rope3d_apply_append(q, k, v, k_ring, v_ring, tables, frames, height, width,
-                        start_frame, token_offset, sink, window):
+                        start_frame, token_offset, sink, window, block_h=0, block_w=0):
     """Causal-RoPE on a token slice, then the write into the ring.
 
     [YL] Algorithm 3 steps 2, 3 and 5 with the cache row replaced by the
@@ -87,7 +108,8 @@ def rope3d_apply_append(q, k, v, k_ring, v_ring, tables, frames, height, width,
     Returns the rotated q.
     """
     n = q.shape[1]
-    pos = positions(frames, height, width, start_frame, token_offset, n, sink, window)
+    pos = positions(frames, height, width, start_frame, token_offset, n, sink, window,
+                    block_h, block_w)
     if k_ring.shape[1] < (sink + window) * height * width:
         raise ValueError("ring smaller than (sink + window) frames")
     k_ring[:, pos[:, 3]] = rope3d.rope3d_apply(k, tables, pos)

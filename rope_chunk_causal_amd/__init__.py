@@ -47,7 +47,8 @@ class rcc_grid(ctypes.Structure):
 
 
 class rcc_ring(ctypes.Structure):
-    _fields_ = [("sink_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32)]
+    _fields_ = [("sink_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
+                ("block_h", ctypes.c_int32), ("block_w", ctypes.c_int32)]
 
 
 def rope_cfg(d_t, d_h, d_w, max_t, max_h, max_w, theta=10000.0) -> rcc_rope3d_cfg:
@@ -58,8 +59,8 @@ def grid(frames, height, width, start_frame, token_offset=0) -> rcc_grid:
     return rcc_grid(frames, height, width, start_frame, token_offset)
 
 
-def ring(sink_frames, window_frames) -> rcc_ring:
-    return rcc_ring(sink_frames, window_frames)
+def ring(sink_frames, window_frames, block_h=0, block_w=0) -> rcc_ring:
+    return rcc_ring(sink_frames, window_frames, block_h, block_w)
 
 
 _lib: Optional[ctypes.CDLL] = None

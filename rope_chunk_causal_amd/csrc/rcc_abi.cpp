@@ -64,6 +64,9 @@ rcc_status check_grid(const rcc_grid* g, int64_t n_tokens, rcc::GridArgs* out) {
   out->token_offset = (int32_t)g->token_offset;
   out->sink = 0;
   out->window = 0;
+  out->block_h = 0;
+  out->block_w = 0;
+  out->blocks_w = 0;
   return RCC_OK;
 }
 
@@ -78,6 +81,14 @@ rcc_status check_ring(const rcc_grid* g, const rcc_ring* r, rcc::GridArgs* out,
                 r->window_frames, g->frames);
   const int64_t rows = ((int64_t)r->sink_frames + r->window_frames) * out->hw;
   if (rows > kI32Max) return fail(RCC_ERR_SHAPE, "ring rows must be < 2^31");
+  if (r->block_h || r->block_w) {
+    if (r->block_h <= 0 || r->block_w <= 0 || g->height % r->block_h || g->width % r->block_w)
+      return fail(RCC_ERR_SHAPE, "blocks %dx%d must be positive and divide the %dx%d frame",
+                  r->block_h, r->block_w, g->height, g->width);
+    out->block_h = r->block_h;
+    out->block_w = r->block_w;
+    out->blocks_w = g->width / r->block_w;
+  }
   out->sink = r->sink_frames;
   out->window = r->window_frames;
   *ring_rows = rows;

@@ -23,6 +23,8 @@ struct GridArgs {
   int32_t start_frame;        // s
   int32_t token_offset;       // Delta
   int32_t sink, window;       // ring layout (window 0 = no ring)
+  int32_t block_h, block_w;   // blockified frames (0 = row-major)
+  int32_t blocks_w;           // W / block_w
 };
 
 struct TokenPos {
@@ -30,9 +32,11 @@ struct TokenPos {
 };
 
 // i_global = Delta + i; frame in chunk = i_global / HW; t_global = s + frame;
-// h, w in row-major order.  Cache row = slot(t_global) * HW + h*W + w, with
+// h, w in row-major order.  Cache row = slot(t_global) * HW + frame row, with
 // slot(t) = t for the plain cache (so row = s*HW + i_global) and, for the
-// ring, t below the sinks or sink + (t - sink) mod window.
+// ring, t below the sinks or sink + (t - sink) mod window; the frame row is
+// h*W + w, or for blockified frames the block's index times block_h*block_w
+// plus the token's row-major index inside its block.
 __device__ __forceinline__ TokenPos token_position(const GridArgs& g, int32_t i) {
   const uint32_t ig = (uint32_t)(g.token_offset + i);
   const uint32_t f = ig / (uint32_t)g.hw;
@@ -45,7 +49,13 @@ __device__ __forceinline__ TokenPos token_position(const GridArgs& g, int32_t i)
   int32_t slot = p.t;
   if (g.window > 0 && p.t >= g.sink)
     slot = g.sink + (int32_t)((uint32_t)(p.t - g.sink) % (uint32_t)g.window);
-  p.row = slot * g.hw + (int32_t)rem;
+  uint32_t frow = rem;
+  if (g.block_h > 0) {
+    const uint32_t hb = h / (uint32_t)g.block_h, wb = (uint32_t)p.w / (uint32_t)g.block_w;
+    const uint32_t dh = h - hb * (uint32_t)g.block_h, dw = (uint32_t)p.w - wb * (uint32_t)g.block_w;
+    frow = ((hb * (uint32_t)g.blocks_w + wb) * (uint32_t)g.block_h + dh) * (uint32_t)g.block_w + dw;
+  }
+  p.row = slot * g.hw + (int32_t)frow;
   return p;
 }
 

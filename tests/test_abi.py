@@ -160,12 +160,15 @@ def test_qkv_host_checks(kw, status):
 ])
 def test_ring_held_tokens(F, H, W, s, sink, window, held):
     assert rcc.ring_held_tokens(rcc.grid(F, H, W, s), rcc.ring(sink, window)) == held
+    if H % 2 == 0:    # blockifying frames does not change what is held
+        assert rcc.ring_held_tokens(rcc.grid(F, H, W, s), rcc.ring(sink, window, 2, 1)) == held
 
 
 def test_ring_held_tokens_rejects_bad_rings():
     L = rcc.lib()
     g = rcc.grid(3, 2, 2, 0)
-    for r in (rcc.ring(0, 2), rcc.ring(-1, 5), rcc.ring(1 << 30, 1 << 30)):
+    for r in (rcc.ring(0, 2), rcc.ring(-1, 5), rcc.ring(1 << 30, 1 << 30), rcc.ring(0, 3, 2, 0),
+              rcc.ring(0, 3, 0, 2), rcc.ring(0, 3, -2, 2), rcc.ring(0, 3, 2, 3)):
         assert L.rcc_ring_held_tokens(ctypes.byref(g), ctypes.byref(r)) == -1
     assert L.rcc_ring_held_tokens(ctypes.byref(g), None) == -1
 
@@ -175,6 +178,7 @@ def test_ring_held_tokens_rejects_bad_rings():
     (dict(ring=None), rcc.RCC_ERR_NULL),
     (dict(ring=rcc.ring(0, 1)), rcc.RCC_ERR_SHAPE),                     # window < F
     (dict(ring=rcc.ring(-1, 4)), rcc.RCC_ERR_SHAPE),
+    (dict(ring=rcc.ring(1, 3, 3, 4)), rcc.RCC_ERR_SHAPE),                # 3 does not divide 4
     (dict(cache=4 * 16 - 1), rcc.RCC_ERR_RANGE),                        # smaller than the ring
     (dict(grid=rcc.grid(2, 4, 4, 15, 0)), rcc.RCC_ERR_RANGE),            # s + F > max_t
     (dict(grid=rcc.grid(2, 4, 4, 0, 1)), rcc.RCC_ERR_RANGE),             # Delta + n > FHW

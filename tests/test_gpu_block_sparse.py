@@ -144,3 +144,61 @@ def test_errors_reported_without_launch():
                               lists, 0.1)
     assert e.value.status == rcc.RCC_ERR_DTYPE
     assert bool((out == 3.0).all())
+
+
+@pytest.mark.parametrize("bh,bw", [(0, 0), (8, 8), (4, 16)])
+def test_block_sparse_over_a_rolling_ring(bh, bw):
+    """The pieces together: RoPE + ring write for a rollout (1 sink frame, 4
+    window frames), then block-sparse attention of the last chunk over the
+    ring, its sink blocks persistent and a random local subset of the window
+    (always its own blocks).  Frames of 8 x 16 patches are two 64-token
+    blocks each, so the held ring is 10 blocks: runs of 64 row-major tokens,
+    or spatial 8 x 8 / 4 x 16 tiles when the ring write blockifies frames."""
+    t = torch()
+    from oracle import ring as G
+    from oracle import rope3d as R
+    d, nh, F, H, W, sink, window, blk = (44, 42, 42), 2, 2, 8, 16, 1, 4, 64
+    D, hw = 128, 128
+    cfg = rcc.rope_cfg(*d, 32, 8, 16)
+    tables = rcc.rope3d_tables(cfg)
+    otab = R.rope3d_tables(*d, 10000.0, 32, 8, 16)
+    cap = (sink + window) * hw
+    kr = t.zeros((1, cap, nh, D), dtype=t.bfloat16, device="cuda")
+    vr = t.zeros_like(kr)
+    okr, ovr = np.zeros((1, cap, nh, D)), np.zeros((1, cap, nh, D))
+    r = rcc.ring(sink, window, bh, bw)
+    for c in range(6):                                   # frames 0..11: the window wraps
+        s = c * F
+        host = [synth.normal((1, F * hw, nh, D), 700 + 10 * c + i, "bf16") for i in range(3)]
+        dq, dk, dv = (to_dev(x, "bf16") for x in host)
+        qo = t.empty_like(dq)
+        say("ring + sparse: write chunk", c)
+        rcc.rope3d_apply_append_ring(cfg, tables, rcc.grid(F, H, W, s, 0), r, dq, dk, dv, qo,
+                                     kr, vr)
+        q, k, v = (synth.to_f64(x, "bf16") for x in host)
+        oq = G.rope3d_apply_append(q, k, v, okr, ovr, otab, F, H, W, s, 0, sink, window, bh, bw)
+    held = rcc.ring_held_tokens(rcc.grid(F, H, W, 10), r)
+    assert held == cap
+    n_kb, n_qb = held // blk, F * hw // blk
+    own = G.frame_slot(np.arange(10, 12), sink, window)          # slots of the chunk's frames
+    own_blocks = (own[:, None] * (hw // blk) + np.arange(hw // blk)[None, :]).reshape(-1)
+    # query block i of the chunk: its 64 tokens in the ring's row order
+    qrows = G.positions(F, H, W, 10, 0, F * hw, sink, window, bh, bw)[:, 3]
+    perm = np.argsort(qrows)                     # chunk token of each ring-ordered row
+    qo = qo[:, t.from_numpy(perm).cuda()].contiguous()
+    oq = oq[:, perm]
+    g = np.random.Generator(np.random.PCG64(5))
+    persist = np.tile(np.arange(sink * hw // blk, dtype=np.int32), (1, nh, 1))
+    local = np.empty((1, nh, n_qb, 3), dtype=np.int32)
+    for h in range(nh):
+        for i in range(n_qb):
+            local[0, h, i] = [own_blocks[i], *g.choice(np.arange(sink * hw // blk, n_kb), 2)]
+    out = t.full_like(qo, float("nan"))
+    say("ring + sparse: attention")
+    rcc.block_sparse_attn(qo, kr, vr, out, held, blk, t.from_numpy(persist).cuda(),
+                          t.from_numpy(local).cuda(), 1.0 / math.sqrt(D))
+    t.cuda.synchronize()
+    bf = lambda x: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float64)
+    ref = S.block_sparse_attention(bf(oq), bf(okr), ovr, held, blk, persist, local,
+                                   1.0 / math.sqrt(D))
+    check_attn(to_host_f64(out), ref, "ring + block-sparse")

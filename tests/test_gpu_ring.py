@@ -27,18 +27,21 @@ def _bf16(x64: np.ndarray) -> np.ndarray:
     return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x64.astype(np.float32))).astype(np.float64)
 
 
-@pytest.mark.parametrize("F,H,W,s,off,n,sink,window", [
-    (3, 30, 52, 237, 0, 4680, 0, 21),        # last chunk of a 1 min rollout
-    (3, 30, 52, 237, 2 * 585, 585, 3, 18),   # one SP rank's slice, with sinks
-    (2, 4, 5, 0, 0, 40, 1, 4),               # sink frame written
-    (2, 4, 5, 9, 7, 20, 1, 4),
-    (1, 3, 3, 1000, 0, 9, 5, 1),             # window of one frame
+@pytest.mark.parametrize("F,H,W,s,off,n,sink,window,bh,bw", [
+    (3, 30, 52, 237, 0, 4680, 0, 21, 0, 0),        # last chunk of a 1 min rollout
+    (3, 30, 52, 237, 2 * 585, 585, 3, 18, 0, 0),   # one SP rank's slice, with sinks
+    (2, 4, 5, 0, 0, 40, 1, 4, 0, 0),               # sink frame written
+    (2, 4, 5, 9, 7, 20, 1, 4, 0, 0),
+    (1, 3, 3, 1000, 0, 9, 5, 1, 0, 0),             # window of one frame
+    (3, 32, 56, 57, 0, 5376, 3, 12, 8, 8),         # [1,8,8] blocks of a 896x512 frame
+    (3, 32, 56, 57, 1000, 1337, 0, 6, 4, 8),       # a slice, non-square blocks
+    (2, 6, 9, 4, 5, 90, 1, 3, 3, 3),
 ])
-def test_ring_positions_bit_exact(F, H, W, s, off, n, sink, window):
-    say("ring positions", F, H, W, s, off, n, sink, window)
-    got = rcc.ring_positions(rcc.grid(F, H, W, s, off), rcc.ring(sink, window), n)
+def test_ring_positions_bit_exact(F, H, W, s, off, n, sink, window, bh, bw):
+    say("ring positions", F, H, W, s, off, n, sink, window, bh, bw)
+    got = rcc.ring_positions(rcc.grid(F, H, W, s, off), rcc.ring(sink, window, bh, bw), n)
     torch().cuda.synchronize()
-    ref = G.positions(F, H, W, s, off, n, sink, window)
+    ref = G.positions(F, H, W, s, off, n, sink, window, bh, bw)
     assert np.array_equal(got.cpu().numpy().astype(np.int64), ref)
 
 
@@ -159,8 +162,10 @@ def test_480p_long_rollout_ring_sampled(name, sink, window, last):
     check_attn(to_host_f64(out[:, tok]), ref, f"{name} attn")
 
 
-def test_qkv_ring_write():
-    """Fused projection into the ring: rollout of 6 chunks over a 1 + 3 frame ring."""
+@pytest.mark.parametrize("bh,bw", [(0, 0), (2, 5)])
+def test_qkv_ring_write(bh, bw):
+    """Fused projection into the ring: rollout of 6 chunks over a 1 + 3 frame
+    ring, frames row-major or blockified into 2 x 5 tiles."""
     t = torch()
     d, nh, F, H, W, sink, window, K = (12, 10, 10), 2, 2, 4, 5, 1, 3, 64
     D, hw = 32, 20
@@ -180,12 +185,14 @@ def test_qkv_ring_write():
             xb = synth.normal((1, n, K), 40 + 10 * c + off, "bf16")
             qo = t.empty((1, n, nh, D), dtype=t.bfloat16, device="cuda")
             say("qkv ring chunk", c, "slice", off, n)
-            rcc.qkv_rope_append_ring(cfg, tables, rcc.grid(F, H, W, s, off), rcc.ring(sink, window),
-                                     to_dev(xb, "bf16"), w, bdev, qo, kr, vr)
+            rcc.qkv_rope_append_ring(cfg, tables, rcc.grid(F, H, W, s, off),
+                                     rcc.ring(sink, window, bh, bw), to_dev(xb, "bf16"), w, bdev,
+                                     qo, kr, vr)
             t.cuda.synchronize()
             q, k, v = Q.qkv_project(synth.to_f64(xb, "bf16"), synth.to_f64(wb, "bf16"),
                                     bias.astype(np.float64), nh, D)
-            oq = G.rope3d_apply_append(q, k, v, okr, ovr, otab, F, H, W, s, off, sink, window)
+            oq = G.rope3d_apply_append(q, k, v, okr, ovr, otab, F, H, W, s, off, sink, window,
+                                       bh, bw)
             check_bf16_rope(to_host_f64(qo), oq, f"c{c} q'")
         check_bf16_rope(to_host_f64(kr), okr, f"c{c} k ring")
         check_bf16_rope(to_host_f64(vr), ovr, f"c{c} v ring")

@@ -134,6 +134,17 @@ def _mut_held_no_sinks(F, s, sink, window):
     return h[h >= sink]
 
 
+_orig_frame_row = G.frame_row
+
+
+def _mut_frame_row_block_transposed(h, w, H, W, bh=0, bw=0):
+    if not bh:
+        return _orig_frame_row(h, w, H, W)
+    h, w = np.asarray(h), np.asarray(w)
+    block = (h // bh) * (W // bw) + w // bw
+    return block * (bh * bw) + (w % bw) * bh + h % bh
+
+
 def _mut_ring_time_is_slot(F, H, W, s, off, n, sink, window):
     p = _orig_ring_positions(F, H, W, s, off, n, sink, window).copy()
     p[:, 0] = p[:, 3] // (H * W)
@@ -183,6 +194,7 @@ RING_PINS = [
     (TG.test_rolled_rollout_matches_brute_force_over_a_full_cache, (1, 4, 3)),
     (TG.test_time_shift_moves_slots_not_outputs, ()),
     (TG.test_sinks_survive_and_memory_is_bounded, ()),
+    (TG.test_blockified_frame_rows, (4, 6, 2, 3)),
 ]
 
 SPARSE_PINS = [
@@ -234,6 +246,7 @@ def test_qkv_mutant_is_caught(monkeypatch, mutant):
     ("held_frames", _mut_held_one_short),
     ("held_frames", _mut_held_no_sinks),
     ("positions", _mut_ring_time_is_slot),
+    ("frame_row", _mut_frame_row_block_transposed),
 ])
 def test_ring_mutant_is_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(G, attr, mutant)

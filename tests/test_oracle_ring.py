@@ -203,11 +203,53 @@ def test_sharded_writes_compose():
     np.testing.assert_array_equal(v2, v1)
 
 
+@pytest.mark.parametrize("H,W,bh,bw", [(8, 16, 8, 8), (4, 6, 2, 3), (6, 4, 1, 4), (4, 4, 4, 4)])
+def test_blockified_frame_rows(H, W, bh, bw):
+    """Blockify: a permutation of each frame's rows in which every (bh x bw)
+    tile occupies consecutive rows, tiles in row-major order, tokens
+    row-major inside a tile (brute-force enumeration)."""
+    rows = {}
+    expect_block = 0
+    for hb in range(H // bh):
+        for wb in range(W // bw):
+            members = [(hb * bh + dh, wb * bw + dw) for dh in range(bh) for dw in range(bw)]
+            for j, (h, w) in enumerate(members):
+                rows[(h, w)] = expect_block * bh * bw + j
+            expect_block += 1
+    got = {(h, w): int(G.frame_row(h, w, H, W, bh, bw)) for h in range(H) for w in range(W)}
+    assert got == rows
+    assert sorted(got.values()) == list(range(H * W))
+    p = G.positions(2, H, W, 6, 3, 2 * H * W - 3, 1, 3, bh, bw)
+    plain = G.positions(2, H, W, 6, 3, 2 * H * W - 3, 1, 3)
+    np.testing.assert_array_equal(p[:, :3], plain[:, :3])
+    np.testing.assert_array_equal(p[:, 3] // (H * W), plain[:, 3] // (H * W))   # same slots
+
+
+def test_blockify_leaves_ring_attention_unchanged():
+    """Blockify only permutes rows inside the held frames: attention over the
+    held memory is the same up to rounding."""
+    d = (4, 4, 4)
+    nh, D, F, H, W, sink, window = 2, 12, 2, 4, 4, 1, 3
+    tables = R.rope3d_tables(*d, 10000.0, 64, 4, 4)
+    outs = []
+    for bh, bw in ((0, 0), (2, 2)):
+        cap = (sink + window) * H * W
+        kr, vr = np.zeros((1, cap, nh, D)), np.zeros((1, cap, nh, D))
+        for c in range(5):
+            q, k, v = (_rand((1, F * H * W, nh, D), 40 + 3 * c + i) for i in range(3))
+            qr = G.rope3d_apply_append(q, k, v, kr, vr, tables, F, H, W, c * F, 0, sink, window,
+                                       bh, bw)
+        outs.append(G.ring_attention(qr, kr, vr, F, H, W, (5 - 1) * F, sink, window, 0.3))
+    np.testing.assert_allclose(outs[0], outs[1], rtol=0, atol=1e-13)
+
+
 def test_errors():
     with pytest.raises(ValueError):
         G.held_frames(3, 0, 0, 2)            # window smaller than a chunk
     with pytest.raises(ValueError):
         G.positions(1, 2, 2, 0, 0, 4, -1, 3)
+    with pytest.raises(ValueError):
+        G.positions(1, 4, 6, 0, 0, 4, 0, 3, 4, 4)       # 4 does not divide 6
     with pytest.raises(ValueError):
         G.rope3d_apply_append(np.zeros((1, 4, 1, 12)), np.zeros((1, 4, 1, 12)),
                               np.zeros((1, 4, 1, 12)), np.zeros((1, 4, 1, 12)),
