@@ -49,10 +49,19 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of what the attention kernels are compiled from: their sources,
+    and from the shared internal header the vector typedefs and the
+    attention argument struct (the rest of that header serves other
+    kernels)."""
+    import re
+    csrc = os.path.join(ROOT, "rope_chunk_causal_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("attn.hip", "attn_d128.hip", "attn_tile.h", "rcc_internal.h"):
-        with open(os.path.join(ROOT, "rope_chunk_causal_amd", "csrc", f), "rb") as fh:
+    for f in ("attn.hip", "attn_d128.hip", "attn_tile.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    text = open(os.path.join(csrc, "rcc_internal.h")).read()
+    for m in re.finditer(r"^typedef [^\n]*;$|^struct AttnArgs \{.*?^\};", text, re.M | re.S):
+        h.update(m.group(0).encode())
     return h.hexdigest()[:16]
 
 
