@@ -152,7 +152,9 @@ RCC_API rcc_status rcc_rope3d_apply_append(
  * floor(j / chunk_tokens) <= floor((q_pos + i) / chunk_tokens).
  * out = softmax(scale * q k^T over visible keys) v, scale > 0.  Operands are rounded
  * to bf16 (nearest-even) for the matrix cores; accumulation and softmax
- * state are fp32.
+ * state are fp32.  With bf16 inputs and head_dim 128, q is multiplied by
+ * scale * log2(e) in fp32 before that rounding (the scores then leave the
+ * matrix cores in base-2 units, ready for the exponential).
  * Errors: NULL; DTYPE; SHAPE (head_dim not a multiple of 8 in [8, 128],
  * batch/n_heads/chunk_tokens non-positive, q_tokens < 0, scale not positive
  * and finite); RANGE

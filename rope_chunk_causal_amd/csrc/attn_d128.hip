@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
   // loaded before the first K/V tiles so the per-tile waits below count only
   // tile loads.
   bf16x8 qf[8];
-  load_q(qf, qg, rs, qclamp, g);
+  load_q<true>(qf, qg, rs, qclamp, g, a.scale_log2);
 
   const Dma dma = dma_offsets(wave, lane);
   issue_tile(kg, vg, rs, 0, kv_end, dma, sK0, sV0, wave, lane);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
   L.lim = min(a.kv_tokens, ((a.q_pos + qclamp) / C + 1) * C);
 
   WaveState w;
-  wave_init(w);
+  wave_init<true>(w);
   const float c2 = a.scale_log2;
 
   // Tile t lives in stage t % 4; tiles t+1 and t+2 are in flight while it is
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
   auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn) {
     tile_ready<4>();
     issue_tile(kg, vg, rs, (t + 3) * kBN, kv_end, dma, kn, vn, wave, lane);
-    tile_step<true>(w, L, qf, ks, vs, t * kBN, lim_lo, c2);
+    tile_step<true, true>(w, L, qf, ks, vs, t * kBN, lim_lo, c2);
   };
   int t = 0;
   for (; t + kStages <= n_tiles; t += kStages) {

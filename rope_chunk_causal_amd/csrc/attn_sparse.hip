@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * NW, NW > 1 ? 2 : 1) void attn_sparse_kernel(Sp
   const int qrow = qb * (32 * NW) + wave * 32 + l32;
   const int qclamp = qrow < a.q_tokens ? qrow : a.q_tokens - 1;
   bf16x8 qf[8];
-  load_q(qf, qg, rs, qclamp, g);
+  load_q<false>(qf, qg, rs, qclamp, g, a.scale_log2);
 
   // ---- the query block's key set: bitmap over key blocks, then compaction
   uint32_t* bm = reinterpret_cast<uint32_t*>(sS0);
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * NW, NW > 1 ? 2 : 1) void attn_sparse_kernel(Sp
   Lane L;
   lane_setup(L, lane);
   WaveState w;
-  wave_init(w);
+  wave_init<false>(w);
   const float c2 = a.scale_log2;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
 
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64 * NW, NW > 1 ? 2 : 1) void attn_sparse_kernel(Sp
       const int un = (u + S - 1) % S;
       issue_sparse<NW>(kg, vg, row_bytes, s_list, t + S - 1, n_tiles, stage(un),
                        stage(un) + kTileBytes, wave, lane);
-      tile_step<false>(w, L, qf, stage(u), stage(u) + kTileBytes, 0, 0, c2);
+      tile_step<false, false>(w, L, qf, stage(u), stage(u) + kTileBytes, 0, 0, c2);
     };
     int t = 0;
     for (; t + S <= n_tiles; t += S) {
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
   const int qrow = (qb0 + jw) * B + wq * 32 + l32;
   const int qclamp = qrow < a.q_tokens ? qrow : a.q_tokens - 1;
   bf16x8 qf[8];
-  load_q(qf, qg, rs, qclamp, g);
+  load_q<false>(qf, qg, rs, qclamp, g, a.scale_log2);
 
   // ---- key sets: persistent bitmap, then per query block the local blocks
   // not already persistent; compacted into ascending lists.
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
   Lane L;
   lane_setup(L, lane);
   WaveState w;
-  wave_init(w);
+  wave_init<false>(w);
   const float c2 = a.scale_log2;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
 
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
     auto step = [&](int t, int u) {
       tile_ready<4>();
       issue_p(t + 3, stage((u + 3) & 3));
-      tile_step<false>(w, L, qf, stage(u), stage(u) + kTileBytes, 0, 0, c2);
+      tile_step<false, false>(w, L, qf, stage(u), stage(u) + kTileBytes, 0, 0, c2);
     };
     int t = 0;
     for (; t + 4 <= n_pt; t += 4) {
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
       auto step = [&](int t, int u) {
         tile_ready<kLWait>();
         issue_l(t + SL - 1, stage(J * SL + (u + SL - 1) % SL));
-        tile_step<false>(w, L, qf, stage(J * SL + u), stage(J * SL + u) + kTileBytes, 0, 0, c2);
+        tile_step<false, false>(w, L, qf, stage(J * SL + u), stage(J * SL + u) + kTileBytes, 0, 0, c2);
       };
       int t = 0;
       for (; t + SL <= my; t += SL) {

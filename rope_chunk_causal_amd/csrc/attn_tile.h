@@ -67,8 +67,17 @@ __device__ __forceinline__ void tile_ready() {
 }
 
 // Per-wave state carried across key tiles.
+//
+// Two bookkeeping schemes for the scores, chosen per kernel (kBase2):
+// * classic: S^T = K Q^T from the bf16 q; a score's probability is
+//   exp2(s * c2 - m_run) with c2 = scale * log2(e) (one fma per score);
+// * base-2 accumulation: q is pre-multiplied by c2 (load_q<true>) and the
+//   S^T accumulation starts from negm = -m_run, so the MFMA results are
+//   already s * c2 - m_run and a score's probability is exp2 of it, with
+//   no VALU op before the exponential.  It needs 16 more VGPRs (negm).
 struct WaveState {
   f32x16 oacc[4];
+  f32x16 negm;          // -m_run in every element (base-2 scheme only)
   float m_run, l_run;
 };
 
@@ -94,37 +103,53 @@ __device__ __forceinline__ void lane_setup(Lane& L, int lane) {
   }
 }
 
+template <bool kBase2>
 __device__ __forceinline__ void wave_init(WaveState& w) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) w.oacc[dt] = f32x16{};
-  w.m_run = -INFINITY;
+  w.negm = f32x16{};
+  // The base-2 scheme needs a finite reference from the start (it enters the
+  // MFMA accumulation); the first tile with weight moves it to that tile's
+  // max.
+  w.m_run = kBase2 ? 0.f : -INFINITY;
   w.l_run = 0.f;
 }
 
-// Q^T operand fragments of query row `qrow` (the lane's column of S^T).
+// Q^T operand fragments of query row `qrow` (the lane's column of S^T); for
+// the base-2 scheme multiplied by c2 = scale * log2(e) in fp32 and rounded
+// to bf16 (nearest even) once.
+template <bool kBase2>
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[8], const __bf16* qg, int64_t rs, int qrow,
-                                       int g) {
+                                       int g, float c2) {
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    qf[kk] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qrow * rs + kk * 16 + g * 8);
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qrow * rs + kk * 16 + g * 8);
+    if constexpr (kBase2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)((float)x[e] * c2);
+    } else {
+      qf[kk] = x;
+    }
+  }
 }
 
 // One 32-key tile read from stage buffers (ks, vs); later tiles are already
 // being loaded into other stages.  Each stage is a distinct __shared__ object,
 // so the compiler does not order these LDS reads after the other stages' DMA
 // writes.  kMask: keys at or past L.lim get no weight (only tiles that reach
-// lim_lo test it).
-template <bool kMask>
+// lim_lo test it).  kBase2: the score bookkeeping (see WaveState).
+template <bool kMask, bool kBase2>
 __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf16x8 (&qf)[8],
                                           const char* ks, const char* vs, int j0, int lim_lo,
                                           float c2) {
-  // S^T = K Q^T, fragment reads kept ahead of the MFMAs that consume them.
-  f32x16 s0 = f32x16{};
+  // S^T = K Q^T (base 2: K (c2 Q)^T - m_run), fragment reads kept ahead of
+  // the MFMAs that consume them.
   bf16x8 ka[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const bf16x8*>(ks + L.koff[kk]);
+  f32x16 s0 = mfma32(ka[0], qf[0], kBase2 ? w.negm : f32x16{});
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) s0 = mfma32(ka[kk], qf[kk], s0);
+  for (int kk = 1; kk < 8; ++kk) s0 = mfma32(ka[kk], qf[kk], s0);
 
   if constexpr (kMask) {
     if (j0 + kBN > lim_lo) {
@@ -155,24 +180,48 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
 #pragma unroll
   for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);  // v_max3_f32
   mx = fmaxf(mx, s0[15]);
-  mx = xhalf_max(mx) * c2;
-  // Lazy rescale: move the reference max only when it would grow by > 2^8.
-  const float m_use = (mx - w.m_run > kLazy) ? mx : w.m_run;
-  if (__ballot(m_use != w.m_run)) {
-    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
-    w.l_run *= alpha;
+  mx = xhalf_max(mx);
+  if constexpr (kBase2) {
+    // mx is the tile max relative to the reference.  Lazy rescale: move the
+    // reference only when the max would exceed it by more than 2^8, or,
+    // before the row has any weight, to the first finite max (so that very
+    // negative scores do not all underflow).
+    const bool move = mx > kLazy || (w.l_run == 0.f && mx > -INFINITY);
+    if (__ballot(move)) {
+      const float shift = move ? mx : 0.f;
+      const float alpha = w.l_run == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
+      w.l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
-    w.m_run = m_use;
+        for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] -= shift;
+      w.m_run += shift;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.negm[r] = -w.m_run;
+    }
+  } else {
+    mx *= c2;
+    // Lazy rescale: move the reference max only when it would grow by > 2^8.
+    const float m_use = (mx - w.m_run > kLazy) ? mx : w.m_run;
+    if (__ballot(m_use != w.m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
+      w.l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
+      w.m_run = m_use;
+    }
   }
 
   float rsum = 0.f;
   bf16x8 pf[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -w.m_run));
+    const float p = kBase2 ? __builtin_amdgcn_exp2f(s0[r])
+                           : __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -w.m_run));
     rsum += p;
     pf[r >> 3][r & 7] = (__bf16)p;
   }
