@@ -169,8 +169,6 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
-    # the shader clock while these steps run (they are all queued already)
-    clocks = sample_gfx_clock(evs[-1][2])
     torch.cuda.synchronize()
     rope_all = sorted(e[0].elapsed_time(e[1]) for e in evs)
     attn_all = sorted(e[1].elapsed_time(e[2]) for e in evs)
@@ -235,7 +233,6 @@ def main():
         "attn_ms": round(attn_ms, 4),
         "attn_ms_median": round(attn_all[len(attn_all) // 2], 4),
         "attn_ms_min": round(attn_all[0], 4),
-        "gfx_clock_mhz_amdsmi": clocks,
         "attn_tflops": round(attn_tflops, 2),
         "rope_ms": round(rope_ms, 4),
         "rope_gbps": round(rope_gbps, 1),
@@ -257,48 +254,6 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows, wl, s, kv, scale)
     print(json.dumps(result), flush=True)
-
-
-def sample_gfx_clock(done_event, period_s=0.002, max_samples=200):
-    """Shader clock (MHz, mean over XCDs) as amdsmi's GPU metrics report it,
-    sampled until done_event completes; None where amdsmi is unavailable.
-    The metrics table updates coarsely (it read a constant 2070 MHz over a
-    40 ms run where the kernel's own s_memtime stamps averaged 1930 MHz), so
-    this is a coarse record of the clock state, not a precise measurement."""
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
-    except Exception:
-        return None
-
-    def read():
-        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-        cur = m.get("current_gfxclks")
-        vals = [x for x in cur if isinstance(x, int) and 0 < x < 10000] if isinstance(cur, list) else []
-        if vals:
-            return sum(vals) / len(vals)
-        avg = m.get("average_gfxclk_frequency")
-        return float(avg) if isinstance(avg, int) and 0 < avg < 10000 else None
-
-    samples = []
-    try:
-        while not done_event.query() and len(samples) < max_samples:
-            v = read()
-            if v is not None:
-                samples.append(v)
-            time.sleep(period_s)
-    except Exception:
-        pass
-    finally:
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
-    if not samples:
-        return None
-    return {"mean": round(sum(samples) / len(samples), 1), "min": round(min(samples), 1),
-            "max": round(max(samples), 1), "samples": len(samples)}
 
 
 def _time_events(fn, stream, reps):
