@@ -204,6 +204,23 @@ def main():
     sp_ms = sum(sp_ev[i].elapsed_time(sp_ev[i + 1]) for i in range(reps)) / reps
     sp_bytes = 6.0 * B_sp * n_sp * nh * D * 2
     sp_gbps = sp_bytes / (sp_ms * 1e-3) / 1e9
+    del sp_sets
+    # Reference: a plain device-to-device copy (torch copy_) moving the same
+    # bytes (half read, half written), two rotating buffer pairs.
+    n_el = int(sp_bytes // 4)
+    cp = [(torch.empty(n_el, device=dev, dtype=bf), torch.empty(n_el, device=dev, dtype=bf))
+          for _ in range(2)]
+    for i in range(3):
+        cp[i % 2][1].copy_(cp[i % 2][0])
+    cp_ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    cp_ev[0].record()
+    for i in range(reps):
+        cp[i % 2][1].copy_(cp[i % 2][0])
+        cp_ev[i + 1].record()
+    torch.cuda.synchronize()
+    cp_ms = sum(cp_ev[i].elapsed_time(cp_ev[i + 1]) for i in range(reps)) / reps
+    cp_gbps = 4.0 * n_el / (cp_ms * 1e-3) / 1e9
+    del cp
 
     rollout = rollout_480p(rcc, synth, cfg, tables, randn, stream, dev)
     qkv = qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev)
@@ -237,7 +254,9 @@ def main():
         "rope_ms": round(rope_ms, 4),
         "rope_gbps": round(rope_gbps, 1),
         "rope_sp_shard_b64": {"ms": round(sp_ms, 4), "gbps": round(sp_gbps, 1),
-                              "bytes": sp_bytes, "frac_hbm": round(sp_gbps / PEAK_HBM_GBPS, 4)},
+                              "bytes": sp_bytes, "frac_hbm": round(sp_gbps / PEAK_HBM_GBPS, 4),
+                              "plain_copy_gbps": round(cp_gbps, 1),
+                              "frac_of_plain_copy": round(sp_gbps / cp_gbps, 4)},
         "tables_once_ms": round(tables_ms, 3),
         "rollout_480p": rollout,
         "qkv_rope_append": qkv,

@@ -127,8 +127,9 @@ RCC_API rcc_status rcc_rope3d_positions(const rcc_grid* grid, int64_t n_tokens,
  * coordinate (fp32 arithmetic).  q_out gets rotated q; cache rows
  * s*H*W + Delta + [0, n_tokens) get rotated k and the unrotated v
  * (overwriting them); no other cache row is touched.
- * Errors: NULL; DTYPE; SHAPE (D != d_t + d_h + d_w, D % 8 != 0, batch,
- * n_heads or grid non-positive, n_tokens < 0); RANGE (Delta < 0,
+ * Errors: NULL; DTYPE; SHAPE (D != d_t + d_h + d_w, D % 8 != 0, batch
+ * outside [1, 65535], n_heads or grid non-positive, n_tokens < 0,
+ * n_tokens * n_heads * D / 8 >= 2^31); RANGE (Delta < 0,
  * Delta + n_tokens > F*H*W, s < 0, s + F > max_t, H > max_h, W > max_w,
  * s*H*W + Delta + n_tokens > cache_tokens); ALIGN; HIP.
  */

@@ -148,7 +148,7 @@ rcc_status rope_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const
   if (D % 8) return fail(RCC_ERR_SHAPE, "head_dim %lld is not a multiple of 8", (long long)D);
   if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
   if (n_heads <= 0) return fail(RCC_ERR_SHAPE, "n_heads must be positive");
-  if ((int64_t)n_heads * D > kI32Max || n_tokens * (D / 8) > kI32Max)
+  if ((int64_t)n_heads * D > kI32Max || n_tokens * n_heads * (D / 8) > kI32Max)
     return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");
   if ((st = check_tables_cover(cfg, grid)) != RCC_OK) return st;
   if ((st = check_cache_rows(grid, g, n_tokens, ring_rows, cache_tokens)) != RCC_OK) return st;

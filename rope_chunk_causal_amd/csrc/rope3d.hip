@@ -9,13 +9,14 @@
 //   cache write   Algorithm 3 step 5
 //
 // The apply kernel is HBM-bound: per token it reads q, k, v and writes
-// q', k-cache and v-cache rows (6 * n_heads * D elements).  One thread owns
-// 8 consecutive elements (4 rotary pairs) of a token's head vector; it
-// fetches the 4 (cos, sin) pairs of its slot once from the L2-resident
-// tables and reuses them for kHeadsPerThread heads of q and k, so the
-// table traffic is a small fraction of the streamed bytes.  All loads of a
-// thread are issued before its first store (bytes in flight, and in-place
-// q_out == q stays correct).  Streamed data is read and written with
+// q', k-cache and v-cache rows (6 * n_heads * D elements).  Threads are laid
+// along the [token, head, D] rows: one thread owns one 16-byte chunk (8
+// elements, 4 rotary pairs) of a row, so every wave-wide access covers 1 KB
+// of consecutive bytes of q, k, v and of the cache rows (4.6-5.8% more HBM
+// bandwidth than a thread per (token, slot) looping over heads, whose
+// accesses were 256-byte pieces 3 KB apart).  The 4 (cos, sin) pairs of a
+// chunk come from the L2-resident tables.  All loads of a thread are issued
+// before its first store (in-place q_out == q stays correct).  Streamed data is read and written with
 // non-temporal hints: each byte is touched once here, and keeping it out of
 // the caches measured ~15% more HBM bandwidth than plain accesses.
 #include "rcc_internal.h"
@@ -25,7 +26,6 @@ namespace rcc {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kHeadsPerThread = 2;
 
 // ---------------------------------------------------------------- tables
 
@@ -140,23 +140,24 @@ __device__ __forceinline__ void rotate8(float x[8], const float c[4], const floa
   }
 }
 
-// grid: x = ceil(n_tokens * D/8 / kBlock), y = head groups, z = batch.
+// grid: x = ceil(n_tokens * n_heads * D/8 / kBlock), z = batch; a wave covers
+// 1 KB of consecutive bytes of the [token, head, D] rows.
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(kBlock) void rope3d_apply_append_kernel(RopeArgs a) {
-  const int32_t slots = a.head_dim >> 3;                       // 8-element slots per head
+  const uint32_t slots = (uint32_t)a.head_dim >> 3;
+  const uint32_t row_chunks = (uint32_t)a.n_heads * slots;
   const uint32_t tid = blockIdx.x * kBlock + threadIdx.x;
-  if (tid >= (uint32_t)a.n_tokens * (uint32_t)slots) return;
-  const int32_t i = (int32_t)(tid / (uint32_t)slots);
-  const int32_t c = (int32_t)(tid - (uint32_t)i * (uint32_t)slots);
+  if (tid >= (uint32_t)a.n_tokens * row_chunks) return;
+  const int32_t i = (int32_t)(tid / row_chunks);
+  const uint32_t chunk = tid - (uint32_t)i * row_chunks;
+  const int32_t c = (int32_t)(chunk % slots);
   const int32_t b = blockIdx.z;
   const TokenPos p = token_position(a.grid, i);
-
-  // cos/sin of the 4 pairs of this slot; each pair reads its own band's table.
   const float2* tab = reinterpret_cast<const float2*>(a.tables);
   float cs[4], sn[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int32_t j = 4 * c + q;
+  for (int qq = 0; qq < 4; ++qq) {
+    const int32_t j = 4 * c + qq;
     const float2* src;
     if (j < a.pt) {
       src = tab + (int64_t)p.t * a.pt + j;
@@ -166,47 +167,25 @@ __global__ __launch_bounds__(kBlock) void rope3d_apply_append_kernel(RopeArgs a)
       src = tab + a.off_w + (int64_t)p.w * a.pw + (j - a.pt - a.ph);
     }
     const float2 v = *src;
-    cs[q] = v.x;
-    sn[q] = v.y;
+    cs[qq] = v.x;
+    sn[qq] = v.y;
   }
-
   const int64_t row_stride = (int64_t)a.n_heads * a.head_dim;
-  const int64_t in_base = ((int64_t)b * a.n_tokens + i) * row_stride + 8 * c;
-  const int64_t cache_base = ((int64_t)b * a.cache_tokens + p.row) * row_stride + 8 * c;
-  const Tin* q = reinterpret_cast<const Tin*>(a.q) + in_base;
-  const Tin* k = reinterpret_cast<const Tin*>(a.k) + in_base;
-  const Tin* v = reinterpret_cast<const Tin*>(a.v) + in_base;
-  Tout* qo = reinterpret_cast<Tout*>(a.q_out) + in_base;
-  Tout* kc = reinterpret_cast<Tout*>(a.k_cache) + cache_base;
-  Tout* vc = reinterpret_cast<Tout*>(a.v_cache) + cache_base;
-
-  const int32_t h0 = blockIdx.y * kHeadsPerThread;
-  Vec8<Tin> vq[kHeadsPerThread], vk[kHeadsPerThread], vv[kHeadsPerThread];
-#pragma unroll
-  for (int hh = 0; hh < kHeadsPerThread; ++hh) {
-    if (h0 + hh < a.n_heads) {
-      const int64_t o = (int64_t)(h0 + hh) * a.head_dim;
-      vq[hh].load(q + o);
-      vk[hh].load(k + o);
-      vv[hh].load(v + o);
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < kHeadsPerThread; ++hh) {
-    if (h0 + hh < a.n_heads) {
-      const int64_t o = (int64_t)(h0 + hh) * a.head_dim;
-      float x[8];
-      vq[hh].to_float(x);
-      rotate8(x, cs, sn);
-      store8(qo + o, x);
-      vk[hh].to_float(x);
-      rotate8(x, cs, sn);
-      store8(kc + o, x);
-      copy8<Tin, Tout>(vc + o, vv[hh]);
-    }
-  }
+  const int64_t in_off = ((int64_t)b * a.n_tokens + i) * row_stride + 8 * (int64_t)chunk;
+  const int64_t c_off = ((int64_t)b * a.cache_tokens + p.row) * row_stride + 8 * (int64_t)chunk;
+  Vec8<Tin> vq, vk, vv;
+  vq.load(reinterpret_cast<const Tin*>(a.q) + in_off);
+  vk.load(reinterpret_cast<const Tin*>(a.k) + in_off);
+  vv.load(reinterpret_cast<const Tin*>(a.v) + in_off);
+  float x[8];
+  vq.to_float(x);
+  rotate8(x, cs, sn);
+  store8(reinterpret_cast<Tout*>(a.q_out) + in_off, x);
+  vk.to_float(x);
+  rotate8(x, cs, sn);
+  store8(reinterpret_cast<Tout*>(a.k_cache) + c_off, x);
+  copy8<Tin, Tout>(reinterpret_cast<Tout*>(a.v_cache) + c_off, vv);
 }
-
 }  // namespace
 
 hipError_t launch_rope3d_tables(const rcc_rope3d_cfg& cfg, float* tables, hipStream_t s) {
@@ -231,10 +210,8 @@ hipError_t launch_rope3d_positions(const GridArgs& g, int32_t n, int32_t* thw, h
 hipError_t launch_rope3d_apply_append(const RopeArgs& a, rcc_dtype in, rcc_dtype out,
                                       hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
-  const int64_t threads = (int64_t)a.n_tokens * (a.head_dim / 8);
-  const dim3 grid((uint32_t)((threads + kBlock - 1) / kBlock),
-                  (uint32_t)((a.n_heads + kHeadsPerThread - 1) / kHeadsPerThread),
-                  (uint32_t)a.batch);
+  const int64_t threads = (int64_t)a.n_tokens * a.n_heads * (a.head_dim / 8);
+  const dim3 grid((uint32_t)((threads + kBlock - 1) / kBlock), 1, (uint32_t)a.batch);
   if (in == RCC_BF16 && out == RCC_BF16)
     hipLaunchKernelGGL((rope3d_apply_append_kernel<__bf16, __bf16>), grid, dim3(kBlock), 0, s, a);
   else if (in == RCC_BF16 && out == RCC_F32)
