@@ -136,6 +136,33 @@ def test_apply_append_480p_chunk(in_dt, out_dt):
     assert np.all(gv[:, :rows[0]] == -3.0) and np.all(gv[:, rows[-1] + 1:] == -3.0)
 
 
+@pytest.mark.parametrize("heads,D,dt", [(1, 64, "bf16"), (3, 128, "bf16"), (5, 48, "f32"),
+                                         (7, 24, "f32")])
+def test_apply_append_odd_heads_ragged_tokens(heads, D, dt):
+    """Odd head counts, several head dims, a 51-token slice starting mid-frame
+    (offset 6 of a 5 x 7 frame, crossing the frame boundary) and batch 2: the
+    flat thread -> (token, 16-byte chunk) map must cover every element once
+    with a ragged last workgroup."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name="odd", n_heads=heads, head_dim=D,
+                             frames=2, height=5, width=7)
+    s, off, n = 3, 6, 51
+    say("apply odd heads", heads, D, dt)
+    cfg, host, (qo, kc, vc), cap = _run_apply(wl, s, off, n, 2, dt, dt, 70 + heads)
+    rq, rk, rv, pos = _oracle_apply(cfg, wl, s, off, host, dt, cap)
+    rows = pos[:, 3]
+    gq, gk, gv = to_host_f64(qo), to_host_f64(kc), to_host_f64(vc)
+    if dt == "f32":
+        assert np.abs(gq - rq).max() <= 1e-5
+        assert np.abs(gk[:, rows] - rk).max() <= 1e-5
+    else:
+        check_bf16_rope(gq, rq, "q'")
+        check_bf16_rope(gk[:, rows], rk, "k cache")
+    assert np.array_equal(gv[:, rows], rv)
+    other = np.setdiff1d(np.arange(cap), rows)
+    assert np.all(gk[:, other] == 3.0) and np.all(gv[:, other] == -3.0)
+
+
 def test_sp_shards_bit_equal_unsharded_and_match_oracle():
     """Each of 8 ranks' 585-token slice (Delta = 585 r) equals the unsharded run."""
     t = torch()
