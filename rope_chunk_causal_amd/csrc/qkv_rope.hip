@@ -29,10 +29,10 @@
 // * Both operands are K-contiguous rows (64 B per row per stage) with the
 //   16-byte chunk swizzle c ^ ((row / 4) % 4), which makes the ds_read_b128
 //   fragment reads bank-conflict free.
-// * Epilogue, one 32-token block at a time: bias and rotation in registers,
-//   bf16 results staged through the (then free) LDS ring so that 16 lanes
-//   write each token's 256 B of a wave's 128 features with one 16-byte store
-//   each.
+// * Epilogue, one 32-token block at a time: bias (staged in LDS once) and
+//   rotation in registers, bf16 results staged through the (then free) LDS
+//   ring so that 16 lanes write each token's 256 B of a wave's 128 features
+//   with one 16-byte store each.
 #include "rcc_internal.h"
 
 namespace rcc {
@@ -143,6 +143,12 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   const int hd = a.n_heads * a.head_dim;
   const int n_feat = 3 * hd;
   const int n_tok = a.batch * a.n_tokens;
+  // Bias of the workgroup's 256 features, staged in LDS once (read in the
+  // epilogue, after its barrier): per-block global bias loads exposed their
+  // latency 4 TB times per wave.
+  __shared__ __align__(16) float sBias[kBF];
+  if (threadIdx.x < kBF)
+    sBias[threadIdx.x] = (a.bias && f0 + (int)threadIdx.x < n_feat) ? a.bias[f0 + threadIdx.x] : 0.f;
   const __bf16* w = reinterpret_cast<const __bf16*>(a.w);
   const __bf16* x = reinterpret_cast<const __bf16*>(a.x);
   const int steps = K / kBK;
@@ -214,8 +220,8 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   for (int tb = 0; tb < TB; ++tb) {
     const int m = min(t0 + wt * 32 * TB + tb * 32 + l32, n_tok - 1);
     const TokenPos pos = token_position(a.grid, m - (m / a.n_tokens) * a.n_tokens);
-    // Per 32-feature block, every global load it needs (bias, and cos/sin of
-    // its 8 rotary pairs for the lane's token) is issued before any is used.
+    // Per 32-feature block, the cos/sin of its 8 rotary pairs for the lane's
+    // token are all loaded before any is used.
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
       const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
       f32x4 bias[4];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4)
-        bias[j4] = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + f + j4 * 8 + g * 4) : f32x4{};
+        bias[j4] = *reinterpret_cast<const f32x4*>(sBias + wf * 128 + fb * 32 + j4 * 8 + g * 4);
       float2 cs[4][2];
       if (which < 2) {
 #pragma unroll
