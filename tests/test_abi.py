@@ -257,3 +257,51 @@ def test_block_sparse_host_checks(kw, status):
         a["block"], a["scale"], a["q"], FAKE, FAKE, a["cache"], a["persist"], a["n_p"],
         a["local"], a["n_l"], a["out"], None)
     assert st == status, rcc.lib().rcc_last_error()
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "rcc.h"
+
+int main(void) {
+  rcc_rope3d_cfg cfg = {44, 42, 42, 1024, 64, 128, 10000.0};
+  rcc_grid g = {3, 30, 52, 6, 0};
+  rcc_ring ring = {0, 21, 0, 0};
+  long long floats = (long long)rcc_rope3d_tables_floats(&cfg);
+  long long held = (long long)rcc_ring_held_tokens(&g, &ring);
+  rcc_status st = rcc_chunk_causal_attn(RCC_BF16, RCC_BF16, 1, 12, 128, 4680, 9360, 14040,
+                                        4680, 0.0883883f, NULL, NULL, NULL, 14040, NULL, NULL);
+  printf("%lld %lld %s %d\n", floats, held, rcc_status_string(st),
+         (int)(strlen(rcc_last_error()) > 0));
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c99_and_links():
+    """A plain C99 program includes rcc.h, links librcc.so and makes host-only
+    calls (sizes, ring rows, an argument error): the boundary needs no C++."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists(rcc.LIB_PATH):
+        pytest.skip("gcc or librcc.so missing")
+    work = os.path.join(ROOT, "rope_chunk_causal_amd", "_build", "ctest")
+    os.makedirs(work, exist_ok=True)
+    src, exe = os.path.join(work, "abi.c"), os.path.join(work, "abi")
+    with open(src, "w") as f:
+        f.write(C_PROGRAM)
+    libdir = os.path.dirname(rcc.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src,
+                        "-L", libdir, "-lrcc", "-Wl,-rpath," + libdir, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "rcc.h" not in r.stderr, r.stderr       # no warnings from our header
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    floats, held, status, has_detail = out.stdout.split()
+    assert int(floats) == 2 * (1024 * 22 + 64 * 21 + 128 * 21)
+    assert int(held) == 9 * 1560
+    assert status == "RCC_ERR_NULL" and has_detail == "1"
