@@ -87,7 +87,7 @@ def read_traffic(kernel: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (this build has no multi-GPU path); "
+        print(f"bench.py runs on exactly one GPU (the library has no multi-GPU path); "
               f"got --gpus {args.gpus}", file=sys.stderr)
         sys.exit(2)
 
