@@ -137,7 +137,7 @@ def main():
         st = sets[i % N_SETS]
         if ev is not None:
             ev[0].record(s)
-        rcc.rope3d_apply_append(cfg, tables, grid, st["q"], st["k"], st["v"], st["q_out"],
+        rcc.rope3d_apply_append(tables, grid, st["q"], st["k"], st["v"], st["q_out"],
                                 st["kc"], st["vc"], stream=s)
         if ev is not None:
             ev[1].record(s)
@@ -193,12 +193,12 @@ def main():
                         torch.empty(B_sp, cap_sp, nh, D, device=dev, dtype=bf)])
     g_sp = rcc.grid(sp.frames, sp.height, sp.width, s_sp, 2 * n_sp)
     for i in range(3):
-        rcc.rope3d_apply_append(cfg, tables, g_sp, *sp_sets[i % 2], stream=stream)
+        rcc.rope3d_apply_append(tables, g_sp, *sp_sets[i % 2], stream=stream)
     reps = 20
     sp_ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     sp_ev[0].record(stream)
     for i in range(reps):
-        rcc.rope3d_apply_append(cfg, tables, g_sp, *sp_sets[i % 2], stream=stream)
+        rcc.rope3d_apply_append(tables, g_sp, *sp_sets[i % 2], stream=stream)
         sp_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     sp_ms = sum(sp_ev[i].elapsed_time(sp_ev[i + 1]) for i in range(reps)) / reps
@@ -315,7 +315,7 @@ def qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev):
 
         def fused(i):
             st = sets[i % 2]
-            rcc.qkv_rope_append(cfg, tables, g, st["x"], st["w"], None, st["q"], st["kc"], st["vc"],
+            rcc.qkv_rope_append(tables, g, st["x"], st["w"], None, st["q"], st["kc"], st["vc"],
                                 stream=stream)
 
         def unfused(i):
@@ -324,7 +324,7 @@ def qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev):
             torch.matmul(st["x"], w[:K].t(), out=st["yq"])
             torch.matmul(st["x"], w[K:2 * K].t(), out=st["yk"])
             torch.matmul(st["x"], w[2 * K:].t(), out=st["yv"])
-            rcc.rope3d_apply_append(cfg, tables, g, st["yq"].view(B, n, nh, D),
+            rcc.rope3d_apply_append(tables, g, st["yq"].view(B, n, nh, D),
                                     st["yk"].view(B, n, nh, D), st["yv"].view(B, n, nh, D),
                                     st["q"], st["kc"], st["vc"], stream=stream)
 
@@ -361,7 +361,7 @@ def rollout_480p(rcc, synth, cfg, tables, randn, stream, dev):
         for i, (s, (q, k, v)) in enumerate(steps):
             if ev is not None:
                 ev[i][0].record(stream)
-            rcc.rope3d_apply_append(cfg, tables, rcc.grid(wl.frames, wl.height, wl.width, s, 0),
+            rcc.rope3d_apply_append(tables, rcc.grid(wl.frames, wl.height, wl.width, s, 0),
                                     q, k, v, qo, kc, vc, stream=stream)
             if ev is not None:
                 ev[i][1].record(stream)
@@ -417,10 +417,10 @@ def rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev):
             if ev is not None:
                 ev[i][0].record(stream)
             if use_ring:
-                rcc.rope3d_apply_append_ring(cfg, tables, g, ring, q, k, v, qo, kc, vc,
+                rcc.rope3d_apply_append_ring(tables, g, ring, q, k, v, qo, kc, vc,
                                              stream=stream)
             else:
-                rcc.rope3d_apply_append(cfg, tables, g, q, k, v, qo, kc, vc, stream=stream)
+                rcc.rope3d_apply_append(tables, g, q, k, v, qo, kc, vc, stream=stream)
             if ev is not None:
                 ev[i][1].record(stream)
             if use_ring:
@@ -473,7 +473,7 @@ def rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev):
                 torch.empty(B_sp, ring_rows, nh, D, device=dev, dtype=bf)] for _ in range(2)]
 
     def sp_ring(i):
-        rcc.rope3d_apply_append_ring(cfg, tables, g_sp, ring, *sp_sets[i % 2], stream=stream)
+        rcc.rope3d_apply_append_ring(tables, g_sp, ring, *sp_sets[i % 2], stream=stream)
     for i in range(3):
         sp_ring(i)
     sp_ms = _time_events(sp_ring, stream, 20)

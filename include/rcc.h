@@ -65,8 +65,8 @@ typedef enum { RCC_F32 = 0, RCC_BF16 = 1 } rcc_dtype;
  */
 typedef struct {
   int32_t d_t, d_h, d_w;
-  int32_t max_t, max_h, max_w;
   double theta;
+  int32_t max_t, max_h, max_w;
 } rcc_rope3d_cfg;
 
 /*
@@ -90,17 +90,46 @@ typedef struct {
 RCC_API int64_t rcc_rope3d_tables_floats(const rcc_rope3d_cfg* cfg);
 
 /*
- * rope3d_tables — fill `tables_dev` (rcc_rope3d_tables_floats(cfg) floats,
- * caller-owned) with cos/sin of p * theta_{b,j} for every axis b, position
- * p < max_b and pair j.  Angles and cos/sin are evaluated in fp64 on the
- * device and stored rounded to fp32.  Done once; later calls only read it
- * ([YL] §3.4.1 item 2: cos/sin precomputed into contiguous memory instead
- * of per-call caching; Algorithm 2's `freqs`).
- * Errors: NULL, SHAPE (odd or non-positive band dim, non-positive length,
- * theta <= 0), ALIGN, HIP.
+ * The cos/sin tables of one band layout: a descriptor that binds the cfg to
+ * the device buffer built for it.  The caller owns both the descriptor and
+ * the buffer (`data`, at least rcc_rope3d_tables_floats(&cfg) floats, 16-byte
+ * aligned); the library allocates nothing.  Only rcc_rope3d_tables_init
+ * writes a descriptor: it seals the fields, and every later call checks the
+ * seal and rejects (RCC_ERR_SHAPE, nothing launched) a descriptor that was
+ * not made by init or whose cfg, data or floats changed since, so a call can
+ * never index the buffer with a layout it was not sized for.  The buffer is
+ * immutable after rcc_rope3d_tables_build; one descriptor may serve any
+ * number of threads and streams.
  */
-RCC_API rcc_status rcc_rope3d_tables(const rcc_rope3d_cfg* cfg, float* tables_dev,
-                             hipStream_t stream);
+typedef struct {
+  rcc_rope3d_cfg cfg;
+  float* data;
+  int64_t floats;
+  uint64_t seal;
+} rcc_rope3d_tables;
+
+/*
+ * rope3d_tables_init — host only, launches nothing: check `cfg` and the
+ * buffer and write the sealed descriptor `*out`.
+ * Errors: NULL (cfg, buf_dev or out); SHAPE (odd or non-positive band dim,
+ * non-positive table length, theta not positive and finite, buf_floats <
+ * rcc_rope3d_tables_floats(cfg)); ALIGN (buf_dev not 16-byte aligned).
+ * On error *out is zeroed (an unsealed descriptor).
+ */
+RCC_API rcc_status rcc_rope3d_tables_init(const rcc_rope3d_cfg* cfg, float* buf_dev,
+                                          int64_t buf_floats, rcc_rope3d_tables* out);
+
+/*
+ * rope3d_tables_build — fill the descriptor's buffer with cos/sin of
+ * p * theta_{b,j} for every axis b, position p < max_b and pair j.  Angles
+ * and cos/sin are evaluated in fp64 on the device and stored rounded to
+ * fp32.  Done once; later calls only read it ([YL] §3.4.1 item 2: cos/sin
+ * precomputed into contiguous memory instead of per-call caching;
+ * Algorithm 2's `freqs`).
+ * Errors: NULL; SHAPE (descriptor not sealed by init, or changed); HIP.
+ */
+RCC_API rcc_status rcc_rope3d_tables_build(const rcc_rope3d_tables* tables,
+                                           hipStream_t stream);
 
 /*
  * rope3d_positions — write int32 [n_tokens][4] = {t_global, h, w,
@@ -127,14 +156,16 @@ RCC_API rcc_status rcc_rope3d_positions(const rcc_grid* grid, int64_t n_tokens,
  * coordinate (fp32 arithmetic).  q_out gets rotated q; cache rows
  * s*H*W + Delta + [0, n_tokens) get rotated k and the unrotated v
  * (overwriting them); no other cache row is touched.
- * Errors: NULL; DTYPE; SHAPE (D != d_t + d_h + d_w, D % 8 != 0, batch
- * outside [1, 65535], n_heads or grid non-positive, n_tokens < 0,
- * n_tokens * n_heads * D / 8 >= 2^31); RANGE (Delta < 0,
+ * The band layout (D = d_t + d_h + d_w) is the one `tables` was made for.
+ * Errors: NULL; DTYPE; SHAPE (tables not sealed by rcc_rope3d_tables_init
+ * or changed since, D % 8 != 0, batch outside [1, 65535], n_heads or grid
+ * non-positive, n_tokens < 0, n_tokens * n_heads * D / 8 >= 2^31); RANGE
+ * (Delta < 0,
  * Delta + n_tokens > F*H*W, s < 0, s + F > max_t, H > max_h, W > max_w,
  * s*H*W + Delta + n_tokens > cache_tokens); ALIGN; HIP.
  */
 RCC_API rcc_status rcc_rope3d_apply_append(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     rcc_dtype in_dtype, rcc_dtype out_dtype,
     int32_t batch, int64_t n_tokens, int32_t n_heads,
     const void* q, const void* k, const void* v,
@@ -175,7 +206,8 @@ RCC_API rcc_status rcc_chunk_causal_attn(
  * KV-cache write ([YL] §3.4.1 item 3: QKV projection and Causal-RoPE in one
  * kernel; Algorithm 3 steps 1-3 and 5).  All tensors bf16 except the bias.
  *   x        [batch, n_tokens, model_dim]: the call's token slice.
- *   w_qkv    [3 * n_heads * D, model_dim], D = d_t + d_h + d_w: the rows of
+ *   w_qkv    [3 * n_heads * D, model_dim], D = d_t + d_h + d_w of the
+ *            tables' band layout: the rows of
  *            the q, k and v projections stacked in that order, each group
  *            head-major then head_dim (a fused Linear's weight).
  *   bias     fp32 [3 * n_heads * D], or NULL for none.
@@ -186,13 +218,13 @@ RCC_API rcc_status rcc_chunk_causal_attn(
  * (tables, grid, rows s*H*W + Delta + [0, n_tokens)) and rounded to bf16
  * (nearest-even) once, at the store.  q_out gets rotated q; the cache rows
  * of the slice get rotated k and the unrotated v; nothing else is written.
- * Errors: NULL (bias may be NULL); SHAPE (D != d_t + d_h + d_w, D % 32 != 0,
- * model_dim not a positive multiple of 32, batch, n_heads or grid
+ * Errors: NULL (bias may be NULL); SHAPE (tables not sealed or changed,
+ * D % 32 != 0, model_dim not a positive multiple of 32, batch, n_heads or grid
  * non-positive, n_tokens < 0, x or w_qkv of 4 GiB or more); RANGE (as
  * rope3d_apply_append); ALIGN (16 bytes; bias 4 bytes); HIP.
  */
 RCC_API rcc_status rcc_qkv_rope_append(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     int32_t batch, int64_t n_tokens, int32_t n_heads, int32_t model_dim,
     const void* x, const void* w_qkv, const float* bias,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
@@ -269,7 +301,7 @@ RCC_API rcc_status rcc_ring_positions(const rcc_grid* grid, const rcc_ring* ring
  * (sink < 0, window < F, ring of 2^31 rows or more, invalid block dims).
  */
 RCC_API rcc_status rcc_rope3d_apply_append_ring(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     const rcc_ring* ring, rcc_dtype in_dtype, rcc_dtype out_dtype,
     int32_t batch, int64_t n_tokens, int32_t n_heads,
     const void* q, const void* k, const void* v,
@@ -283,7 +315,7 @@ RCC_API rcc_status rcc_rope3d_apply_append_ring(
  * rcc_rope3d_apply_append_ring.
  */
 RCC_API rcc_status rcc_qkv_rope_append_ring(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     const rcc_ring* ring, int32_t batch, int64_t n_tokens, int32_t n_heads,
     int32_t model_dim, const void* x, const void* w_qkv, const float* bias,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
@@ -339,8 +371,8 @@ RCC_API rcc_status rcc_chunk_causal_attn_ring(
  * (in_dtype not bf16, unknown out_dtype); SHAPE (head_dim != 128,
  * block_tokens not 32, 64, 128 or 256, batch/n_heads non-positive,
  * q_tokens/kv_tokens/n_persist/n_local negative, n_persist + n_local >
- * 1024, kv_tokens / B > 32768, scale not positive and finite, a batch
- * entry's cache of 4 GiB or more); RANGE (kv_tokens > cache_tokens);
+ * 1024, kv_tokens / B > 32768, scale not positive and finite); RANGE
+ * (kv_tokens > cache_tokens);
  * ALIGN (tensors 16 bytes, lists 4 bytes); HIP.
  */
 RCC_API rcc_status rcc_block_sparse_attn(

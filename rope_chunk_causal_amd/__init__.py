@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG_DIR, "librcc.so")
 RCC_OK, RCC_ERR_NULL, RCC_ERR_SHAPE, RCC_ERR_RANGE, RCC_ERR_DTYPE, RCC_ERR_ALIGN, RCC_ERR_HIP = range(7)
 RCC_F32, RCC_BF16 = 0, 1
 
-EXPORTS = ("rcc_rope3d_tables_floats", "rcc_rope3d_tables", "rcc_rope3d_positions",
+EXPORTS = ("rcc_rope3d_tables_floats", "rcc_rope3d_tables_init", "rcc_rope3d_tables_build",
+           "rcc_rope3d_positions",
            "rcc_rope3d_apply_append", "rcc_qkv_rope_append", "rcc_chunk_causal_attn",
            "rcc_ring_held_tokens", "rcc_ring_positions", "rcc_rope3d_apply_append_ring",
            "rcc_qkv_rope_append_ring", "rcc_chunk_causal_attn_ring", "rcc_block_sparse_attn",
@@ -36,8 +37,13 @@ class RccError(RuntimeError):
 
 class rcc_rope3d_cfg(ctypes.Structure):
     _fields_ = [("d_t", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_w", ctypes.c_int32),
-                ("max_t", ctypes.c_int32), ("max_h", ctypes.c_int32), ("max_w", ctypes.c_int32),
-                ("theta", ctypes.c_double)]
+                ("theta", ctypes.c_double),
+                ("max_t", ctypes.c_int32), ("max_h", ctypes.c_int32), ("max_w", ctypes.c_int32)]
+
+
+class rcc_rope3d_tables(ctypes.Structure):
+    _fields_ = [("cfg", rcc_rope3d_cfg), ("data", ctypes.c_void_p), ("floats", ctypes.c_int64),
+                ("seal", ctypes.c_uint64)]
 
 
 class rcc_grid(ctypes.Structure):
@@ -52,7 +58,26 @@ class rcc_ring(ctypes.Structure):
 
 
 def rope_cfg(d_t, d_h, d_w, max_t, max_h, max_w, theta=10000.0) -> rcc_rope3d_cfg:
-    return rcc_rope3d_cfg(d_t, d_h, d_w, max_t, max_h, max_w, float(theta))
+    return rcc_rope3d_cfg(d_t=d_t, d_h=d_h, d_w=d_w, theta=float(theta), max_t=max_t,
+                          max_h=max_h, max_w=max_w)
+
+
+class RopeTables:
+    """A sealed tables descriptor (``desc``) and the device buffer it binds
+    (``buf``, a float32 tensor kept alive here)."""
+
+    def __init__(self, desc: rcc_rope3d_tables, buf):
+        self.desc = desc
+        self.buf = buf
+
+    @property
+    def cfg(self) -> rcc_rope3d_cfg:
+        return self.desc.cfg
+
+    @property
+    def head_dim(self) -> int:
+        c = self.desc.cfg
+        return c.d_t + c.d_h + c.d_w
 
 
 def grid(frames, height, width, start_frame, token_offset=0) -> rcc_grid:
@@ -79,14 +104,17 @@ def lib() -> ctypes.CDLL:
     ringp = ctypes.POINTER(rcc_ring)
     L.rcc_rope3d_tables_floats.argtypes = [cfgp]
     L.rcc_rope3d_tables_floats.restype = I64
-    L.rcc_rope3d_tables.argtypes = [cfgp, P, P]
-    L.rcc_rope3d_tables.restype = ctypes.c_int
+    tabp = ctypes.POINTER(rcc_rope3d_tables)
+    L.rcc_rope3d_tables_init.argtypes = [cfgp, P, I64, tabp]
+    L.rcc_rope3d_tables_init.restype = ctypes.c_int
+    L.rcc_rope3d_tables_build.argtypes = [tabp, P]
+    L.rcc_rope3d_tables_build.restype = ctypes.c_int
     L.rcc_rope3d_positions.argtypes = [gridp, I64, P, P]
     L.rcc_rope3d_positions.restype = ctypes.c_int
-    L.rcc_rope3d_apply_append.argtypes = [cfgp, P, gridp, ctypes.c_int, ctypes.c_int,
+    L.rcc_rope3d_apply_append.argtypes = [tabp, gridp, ctypes.c_int, ctypes.c_int,
                                           I32, I64, I32, P, P, P, P, P, P, I64, P]
     L.rcc_rope3d_apply_append.restype = ctypes.c_int
-    L.rcc_qkv_rope_append.argtypes = [cfgp, P, gridp, I32, I64, I32, I32, P, P, P, P, P, P, I64, P]
+    L.rcc_qkv_rope_append.argtypes = [tabp, gridp, I32, I64, I32, I32, P, P, P, P, P, P, I64, P]
     L.rcc_qkv_rope_append.restype = ctypes.c_int
     L.rcc_chunk_causal_attn.argtypes = [ctypes.c_int, ctypes.c_int, I32, I32, I32,
                                         I64, I64, I64, I64, F, P, P, P, I64, P, P]
@@ -95,10 +123,10 @@ def lib() -> ctypes.CDLL:
     L.rcc_ring_held_tokens.restype = I64
     L.rcc_ring_positions.argtypes = [gridp, ringp, I64, P, P]
     L.rcc_ring_positions.restype = ctypes.c_int
-    L.rcc_rope3d_apply_append_ring.argtypes = [cfgp, P, gridp, ringp, ctypes.c_int, ctypes.c_int,
+    L.rcc_rope3d_apply_append_ring.argtypes = [tabp, gridp, ringp, ctypes.c_int, ctypes.c_int,
                                                I32, I64, I32, P, P, P, P, P, P, I64, P]
     L.rcc_rope3d_apply_append_ring.restype = ctypes.c_int
-    L.rcc_qkv_rope_append_ring.argtypes = [cfgp, P, gridp, ringp, I32, I64, I32, I32,
+    L.rcc_qkv_rope_append_ring.argtypes = [tabp, gridp, ringp, I32, I64, I32, I32,
                                            P, P, P, P, P, P, I64, P]
     L.rcc_qkv_rope_append_ring.restype = ctypes.c_int
     L.rcc_chunk_causal_attn_ring.argtypes = [gridp, ringp, ctypes.c_int, ctypes.c_int, I32, I32,
@@ -175,15 +203,37 @@ def rope3d_tables_floats(cfg: rcc_rope3d_cfg) -> int:
     return n
 
 
-def rope3d_tables(cfg: rcc_rope3d_cfg, tables=None, stream=None):
-    """Fill (or allocate and fill) the fp32 cos/sin table buffer on the GPU."""
+def rope3d_tables_init(cfg: rcc_rope3d_cfg, buf) -> RopeTables:
+    """Seal a descriptor binding `cfg` to the float32 GPU buffer `buf` (host
+    only; the buffer is not filled)."""
     torch = _torch()
-    n = rope3d_tables_floats(cfg)
-    if tables is None:
-        tables = torch.empty(n, dtype=torch.float32, device="cuda")
-    _check(lib().rcc_rope3d_tables(ctypes.byref(cfg), _ptr(tables, "tables", n, torch.float32),
-                                   _stream(stream)), "rope3d_tables")
+    desc = rcc_rope3d_tables()
+    if buf is None or not buf.is_cuda or not buf.is_contiguous() or buf.dtype != torch.float32:
+        raise ValueError("buf must be a contiguous float32 GPU tensor")
+    _check(lib().rcc_rope3d_tables_init(ctypes.byref(cfg), buf.data_ptr(), buf.numel(),
+                                        ctypes.byref(desc)), "rope3d_tables_init")
+    return RopeTables(desc, buf)
+
+
+def rope3d_tables_build(tables: RopeTables, stream=None) -> RopeTables:
+    """Fill the tables' device buffer with cos/sin (once)."""
+    _check(lib().rcc_rope3d_tables_build(ctypes.byref(_desc(tables)), _stream(stream)),
+           "rope3d_tables_build")
     return tables
+
+
+def rope3d_tables(cfg: rcc_rope3d_cfg, buf=None, stream=None) -> RopeTables:
+    """Allocate (unless `buf` is given), seal and fill the cos/sin tables of `cfg`."""
+    torch = _torch()
+    if buf is None:
+        buf = torch.empty(rope3d_tables_floats(cfg), dtype=torch.float32, device="cuda")
+    return rope3d_tables_build(rope3d_tables_init(cfg, buf), stream)
+
+
+def _desc(tables) -> rcc_rope3d_tables:
+    if not isinstance(tables, RopeTables):
+        raise TypeError("tables must come from rope3d_tables / rope3d_tables_init")
+    return tables.desc
 
 
 def rope3d_positions(g: rcc_grid, n_tokens: int, thw=None, stream=None):
@@ -197,11 +247,12 @@ def rope3d_positions(g: rcc_grid, n_tokens: int, thw=None, stream=None):
     return thw
 
 
-def _rope_append_args(cfg, tables, q, k, v, q_out, k_cache, v_cache):
-    torch = _torch()
+def _rope_append_args(tables, q, k, v, q_out, k_cache, v_cache):
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or q_out.shape != q.shape:
         raise ValueError("q, k, v, q_out must share one [B, n, heads, D] shape")
     B, n, nh, D = q.shape
+    if D != tables.head_dim:
+        raise ValueError(f"head_dim {D} is not the tables' d_t + d_h + d_w = {tables.head_dim}")
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or \
             k_cache.shape[0] != B or tuple(k_cache.shape[2:]) != (nh, D):
         raise ValueError("caches must be [B, cache_tokens, heads, D]")
@@ -210,37 +261,39 @@ def _rope_append_args(cfg, tables, q, k, v, q_out, k_cache, v_cache):
         raise TypeError("q/k/v share in_dtype; q_out/k_cache/v_cache share out_dtype")
     cap = k_cache.shape[1]
     numel = B * n * nh * D
-    ntab = rope3d_tables_floats(cfg)
-    return ((_dtype_code(q), _dtype_code(q_out), B, n, nh,
-             _ptr(q, "q", numel), _ptr(k, "k", numel), _ptr(v, "v", numel),
-             _ptr(q_out, "q_out", numel), _ptr(k_cache, "k_cache", B * cap * nh * D),
-             _ptr(v_cache, "v_cache", B * cap * nh * D), cap),
-            _ptr(tables, "tables", ntab, torch.float32))
+    return (_dtype_code(q), _dtype_code(q_out), B, n, nh,
+            _ptr(q, "q", numel), _ptr(k, "k", numel), _ptr(v, "v", numel),
+            _ptr(q_out, "q_out", numel), _ptr(k_cache, "k_cache", B * cap * nh * D),
+            _ptr(v_cache, "v_cache", B * cap * nh * D), cap)
 
 
-def rope3d_apply_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, q, k, v, q_out,
+def rope3d_apply_append(tables: RopeTables, g: rcc_grid, q, k, v, q_out,
                         k_cache, v_cache, stream=None) -> None:
     """q, k, v [B, n, heads, D]; q_out same shape; caches [B, cache_tokens, heads, D]."""
-    args, tab = _rope_append_args(cfg, tables, q, k, v, q_out, k_cache, v_cache)
-    _check(lib().rcc_rope3d_apply_append(ctypes.byref(cfg), tab, ctypes.byref(g), *args,
+    desc = _desc(tables)
+    args = _rope_append_args(tables, q, k, v, q_out, k_cache, v_cache)
+    _check(lib().rcc_rope3d_apply_append(ctypes.byref(desc), ctypes.byref(g), *args,
                                          _stream(stream)), "rope3d_apply_append")
 
 
-def rope3d_apply_append_ring(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, r: rcc_ring, q, k, v,
+def rope3d_apply_append_ring(tables: RopeTables, g: rcc_grid, r: rcc_ring, q, k, v,
                              q_out, k_cache, v_cache, stream=None) -> None:
     """As rope3d_apply_append, writing the rolling-window ring rows of the slice."""
-    args, tab = _rope_append_args(cfg, tables, q, k, v, q_out, k_cache, v_cache)
-    _check(lib().rcc_rope3d_apply_append_ring(ctypes.byref(cfg), tab, ctypes.byref(g),
+    desc = _desc(tables)
+    args = _rope_append_args(tables, q, k, v, q_out, k_cache, v_cache)
+    _check(lib().rcc_rope3d_apply_append_ring(ctypes.byref(desc), ctypes.byref(g),
                                               ctypes.byref(r), *args, _stream(stream)),
            "rope3d_apply_append_ring")
 
 
-def _qkv_args(cfg, tables, x, w_qkv, bias, q_out, k_cache, v_cache):
+def _qkv_args(tables, x, w_qkv, bias, q_out, k_cache, v_cache):
     torch = _torch()
     if x.dim() != 3 or q_out.dim() != 4 or tuple(q_out.shape[:2]) != tuple(x.shape[:2]):
         raise ValueError("x must be [B, n, model_dim] and q_out [B, n, heads, D]")
     B, n, K = x.shape
     nh, D = q_out.shape[2], q_out.shape[3]
+    if D != tables.head_dim:
+        raise ValueError(f"head_dim {D} is not the tables' d_t + d_h + d_w = {tables.head_dim}")
     if tuple(w_qkv.shape) != (3 * nh * D, K):
         raise ValueError("w_qkv must be [3 * heads * D, model_dim]")
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or \
@@ -253,29 +306,29 @@ def _qkv_args(cfg, tables, x, w_qkv, bias, q_out, k_cache, v_cache):
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != 3 * nh * D):
         raise TypeError("bias must be float32 [3 * heads * D] or None")
     cap = k_cache.shape[1]
-    ntab = rope3d_tables_floats(cfg)
-    return ((B, n, nh, K, _ptr(x, "x", B * n * K), _ptr(w_qkv, "w_qkv", 3 * nh * D * K),
-             _ptr(bias, "bias", 3 * nh * D), _ptr(q_out, "q_out", B * n * nh * D),
-             _ptr(k_cache, "k_cache", B * cap * nh * D),
-             _ptr(v_cache, "v_cache", B * cap * nh * D), cap),
-            _ptr(tables, "tables", ntab, torch.float32))
+    return (B, n, nh, K, _ptr(x, "x", B * n * K), _ptr(w_qkv, "w_qkv", 3 * nh * D * K),
+            _ptr(bias, "bias", 3 * nh * D), _ptr(q_out, "q_out", B * n * nh * D),
+            _ptr(k_cache, "k_cache", B * cap * nh * D),
+            _ptr(v_cache, "v_cache", B * cap * nh * D), cap)
 
 
-def qkv_rope_append(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, x, w_qkv, bias, q_out,
+def qkv_rope_append(tables: RopeTables, g: rcc_grid, x, w_qkv, bias, q_out,
                     k_cache, v_cache, stream=None) -> None:
     """x [B, n, model_dim] bf16; w_qkv [3*heads*D, model_dim] bf16; bias fp32
     [3*heads*D] or None; q_out [B, n, heads, D] bf16; caches [B, cache_tokens,
     heads, D] bf16."""
-    args, tab = _qkv_args(cfg, tables, x, w_qkv, bias, q_out, k_cache, v_cache)
-    _check(lib().rcc_qkv_rope_append(ctypes.byref(cfg), tab, ctypes.byref(g), *args,
+    desc = _desc(tables)
+    args = _qkv_args(tables, x, w_qkv, bias, q_out, k_cache, v_cache)
+    _check(lib().rcc_qkv_rope_append(ctypes.byref(desc), ctypes.byref(g), *args,
                                      _stream(stream)), "qkv_rope_append")
 
 
-def qkv_rope_append_ring(cfg: rcc_rope3d_cfg, tables, g: rcc_grid, r: rcc_ring, x, w_qkv, bias,
+def qkv_rope_append_ring(tables: RopeTables, g: rcc_grid, r: rcc_ring, x, w_qkv, bias,
                          q_out, k_cache, v_cache, stream=None) -> None:
     """As qkv_rope_append, writing the rolling-window ring rows of the slice."""
-    args, tab = _qkv_args(cfg, tables, x, w_qkv, bias, q_out, k_cache, v_cache)
-    _check(lib().rcc_qkv_rope_append_ring(ctypes.byref(cfg), tab, ctypes.byref(g),
+    desc = _desc(tables)
+    args = _qkv_args(tables, x, w_qkv, bias, q_out, k_cache, v_cache)
+    _check(lib().rcc_qkv_rope_append_ring(ctypes.byref(desc), ctypes.byref(g),
                                           ctypes.byref(r), *args, _stream(stream)),
            "qkv_rope_append_ring")
 

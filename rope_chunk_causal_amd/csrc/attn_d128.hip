@@ -19,6 +19,8 @@
 // * Workgroups are renumbered so each XCD (dispatch is round-robin over the
 //   8 XCDs) gets a contiguous range of (batch, head, query-tile) work: query
 //   tiles of one head run on one XCD and share its L2 for K/V.
+#include <type_traits>
+
 #include "attn_tile.h"
 
 namespace rcc {
@@ -51,19 +53,20 @@ __device__ __forceinline__ Dma dma_offsets(int wave, int lane) {
 // for rows past kv_end (their scores are masked), and a tile past the end (the
 // pipeline always runs three tiles ahead) re-reads it into a stage no step
 // reads again.  Branch-free, so the compiler tracks which stage each load
-// writes.  Offsets are 32-bit from the (batch, head) base: the host limits a
-// batch's cache to 4 GiB.
-__device__ __forceinline__ void issue_tile(const __bf16* kg, const __bf16* vg, int64_t rs,
+// writes.  The tile's first key (clamped) gives a wave-uniform 64-bit base;
+// each lane adds a 32-bit offset of at most 31 rows, so a batch entry's cache
+// may exceed 4 GiB.
+__device__ __forceinline__ void issue_tile(const char* kg, const char* vg, uint32_t row_bytes,
                                            int j0, int kv_end, const Dma& d, char* ks,
                                            char* vs, int wave, int lane) {
-  j0 = __builtin_amdgcn_readfirstlane(j0);
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const int jb = __builtin_amdgcn_readfirstlane(min(j0, kv_end - 1));
+  const int64_t base = (int64_t)jb * row_bytes;
   const int key = min(j0 + 4 * wave + (lane >> 4), kv_end - 1);
-  const uint32_t row = (uint32_t)key * row_bytes;
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kg) + (row + d.k),
-                                   (lds_void*)(ks + wave * 1024), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vg) + (row + d.v),
-                                   (lds_void*)(vs + wave * 1024), 16, 0, 0);
+  const uint32_t row = (uint32_t)(key - jb) * row_bytes;
+  __builtin_amdgcn_global_load_lds(kg + base + (row + d.k), (lds_void*)(ks + wave * 1024), 16, 0,
+                                   0);
+  __builtin_amdgcn_global_load_lds(vg + base + (row + d.v), (lds_void*)(vs + wave * 1024), 16, 0,
+                                   0);
 }
 
 template <typename Tout>
@@ -93,12 +96,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
 
   const int64_t rs = (int64_t)a.n_heads * kD;
   const __bf16* qg = reinterpret_cast<const __bf16*>(a.q) + (int64_t)b * a.q_tokens * rs + h * kD;
-  const __bf16* kg = reinterpret_cast<const __bf16*>(a.k) + (int64_t)b * a.cache_tokens * rs + h * kD;
-  const __bf16* vg = reinterpret_cast<const __bf16*>(a.v) + (int64_t)b * a.cache_tokens * rs + h * kD;
+  const char* kg = reinterpret_cast<const char*>(
+      reinterpret_cast<const __bf16*>(a.k) + (int64_t)b * a.cache_tokens * rs + h * kD);
+  const char* vg = reinterpret_cast<const char*>(
+      reinterpret_cast<const __bf16*>(a.v) + (int64_t)b * a.cache_tokens * rs + h * kD);
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
   Tout* og = reinterpret_cast<Tout*>(a.out) + (int64_t)b * a.q_tokens * rs + h * kD;
 
   const int q0 = qt * kBM;
   const int qrow = q0 + wave * 32 + l32;
+  // A wave whose 32 rows all lie past q_tokens (the last query tile of a
+  // ragged chunk) still moves its share of every K/V tile and meets every
+  // barrier, but runs no matrix or softmax work.
+  const bool has_rows = q0 + wave * 32 < a.q_tokens;
   const int qclamp = qrow < a.q_tokens ? qrow : a.q_tokens - 1;
   const int C = a.chunk_tokens;
   const int qlast = min(q0 + kBM, a.q_tokens) - 1;
@@ -113,9 +123,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
   load_q<true>(qf, qg, rs, qclamp, g, a.scale_log2);
 
   const Dma dma = dma_offsets(wave, lane);
-  issue_tile(kg, vg, rs, 0, kv_end, dma, sK0, sV0, wave, lane);
-  issue_tile(kg, vg, rs, kBN, kv_end, dma, sK1, sV1, wave, lane);
-  issue_tile(kg, vg, rs, 2 * kBN, kv_end, dma, sK2, sV2, wave, lane);
+  issue_tile(kg, vg, row_bytes, 0, kv_end, dma, sK0, sV0, wave, lane);
+  issue_tile(kg, vg, row_bytes, kBN, kv_end, dma, sK1, sV1, wave, lane);
+  issue_tile(kg, vg, row_bytes, 2 * kBN, kv_end, dma, sK2, sV2, wave, lane);
 
   Lane L;
   lane_setup(L, lane);
@@ -126,22 +136,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
   const float c2 = a.scale_log2;
 
   // Tile t lives in stage t % 4; tiles t+1 and t+2 are in flight while it is
-  // computed, and tile t+3 starts into the stage that tile t-1 used.
-  auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn) {
-    tile_ready<4>();
-    issue_tile(kg, vg, rs, (t + 3) * kBN, kv_end, dma, kn, vn, wave, lane);
-    tile_step<true, true>(w, L, qf, ks, vs, t * kBN, lim_lo, c2);
+  // computed, and tile t+3 starts into the stage that tile t-1 used.  The
+  // loop is instantiated twice: with the tile work, and (for a wave with no
+  // query rows) DMA and barriers only, so neither copy branches per tile.
+  auto sweep = [&](auto work) {
+    auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn) {
+      tile_ready<4>();
+      issue_tile(kg, vg, row_bytes, (t + 3) * kBN, kv_end, dma, kn, vn, wave, lane);
+      if constexpr (decltype(work)::value)
+        tile_step<true, true>(w, L, qf, ks, vs, t * kBN, lim_lo, c2);
+    };
+    int t = 0;
+    for (; t + kStages <= n_tiles; t += kStages) {
+      step(t, sK0, sV0, sK3, sV3);
+      step(t + 1, sK1, sV1, sK0, sV0);
+      step(t + 2, sK2, sV2, sK1, sV1);
+      step(t + 3, sK3, sV3, sK2, sV2);
+    }
+    if (t < n_tiles) step(t, sK0, sV0, sK3, sV3);
+    if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0);
+    if (t + 2 < n_tiles) step(t + 2, sK2, sV2, sK1, sV1);
   };
-  int t = 0;
-  for (; t + kStages <= n_tiles; t += kStages) {
-    step(t, sK0, sV0, sK3, sV3);
-    step(t + 1, sK1, sV1, sK0, sV0);
-    step(t + 2, sK2, sV2, sK1, sV1);
-    step(t + 3, sK3, sV3, sK2, sV2);
-  }
-  if (t < n_tiles) step(t, sK0, sV0, sK3, sV3);
-  if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0);
-  if (t + 2 < n_tiles) step(t + 2, sK2, sV2, sK1, sV1);
+  if (has_rows)
+    sweep(std::true_type{});
+  else
+    sweep(std::false_type{});
   // No load may still be writing this workgroup's LDS when it exits.
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -151,9 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
 }  // namespace
 
 bool attn_d128_supported(const AttnArgs& a, rcc_dtype in) {
-  // K/V loads use 32-bit byte offsets inside one batch entry's cache.
-  const int64_t cache_bytes = (int64_t)a.cache_tokens * a.n_heads * kRowBytes;
-  return in == RCC_BF16 && a.head_dim == kD && cache_bytes <= (int64_t)UINT32_MAX;
+  return in == RCC_BF16 && a.head_dim == kD;
 }
 
 hipError_t launch_attn_d128(const AttnArgs& a, rcc_dtype out, hipStream_t s) {

@@ -31,7 +31,9 @@
 //   softmax work is attn_tile.h's, shared with the dense kernel.
 // * K/V tiles stream global -> LDS with global_load_lds_dwordx4, branch-free
 //   (the tile index is clamped to the last tile, so the wait counts stay
-//   exact), into one __shared__ object per stage.
+//   exact), into one __shared__ object per stage.  A tile's first row gives a
+//   wave-uniform 64-bit base and lanes add 32-bit offsets inside the tile, so
+//   a batch entry's cache may exceed 4 GiB.
 // * Workgroups are numbered XCD-major: the query blocks of one head run on
 //   one XCD and share its L2.
 #include <type_traits>
@@ -66,15 +68,15 @@ __device__ __forceinline__ void issue_sparse(const char* kg, const char* vg, uin
   constexpr int kInstr = 8 / NW;
   t = __builtin_amdgcn_readfirstlane(min(t, n_tiles - 1));
   const int blk = __builtin_amdgcn_readfirstlane(list[t / NW]);
-  const uint32_t row0 = (uint32_t)(blk * (32 * NW) + (t % NW) * 32);
+  const int64_t base = (int64_t)(blk * (32 * NW) + (t % NW) * 32) * row_bytes;
 #pragma unroll
   for (int j = 0; j < kInstr; ++j) {
     const int i = wave + NW * j;
     const int r = 4 * i + (lane >> 4);
-    const uint32_t off = (row0 + (uint32_t)r) * row_bytes;
-    __builtin_amdgcn_global_load_lds(kg + (off + k_chunk(r, lane & 15)),
+    const uint32_t off = (uint32_t)r * row_bytes;
+    __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
                                      (lds_void*)(ks + i * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vg + (off + v_chunk(r, lane & 15)),
+    __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
                                      (lds_void*)(vs + i * 1024), 16, 0, 0);
   }
 }
@@ -341,10 +343,11 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
     t = __builtin_amdgcn_readfirstlane(min(t, n_pt - 1));
     const int blk = __builtin_amdgcn_readfirstlane(s_plist[t / NWB]);
     const int r = 4 * wave + (lane >> 4);
-    const uint32_t off = ((uint32_t)(blk * B + (t % NWB) * 32) + (uint32_t)r) * row_bytes;
-    __builtin_amdgcn_global_load_lds(kg + (off + k_chunk(r, lane & 15)),
+    const int64_t base = (int64_t)(blk * B + (t % NWB) * 32) * row_bytes;
+    const uint32_t off = (uint32_t)r * row_bytes;
+    __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
                                      (lds_void*)(ks + wave * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vg + (off + v_chunk(r, lane & 15)),
+    __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
                                      (lds_void*)(ks + kTileBytes + wave * 1024), 16, 0, 0);
   };
   if (n_pt > 0) {
@@ -380,15 +383,15 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
     auto issue_l = [&](int t, char* ks) {
       t = __builtin_amdgcn_readfirstlane(min(t, my - 1));
       const int blk = __builtin_amdgcn_readfirstlane(list[t / NWB]);
-      const uint32_t row0 = (uint32_t)(blk * B + (t % NWB) * 32);
+      const int64_t base = (int64_t)(blk * B + (t % NWB) * 32) * row_bytes;
 #pragma unroll
       for (int jj = 0; jj < 8 / NWB; ++jj) {
         const int i = wq + NWB * jj;
         const int r = 4 * i + (lane >> 4);
-        const uint32_t off = (row0 + (uint32_t)r) * row_bytes;
-        __builtin_amdgcn_global_load_lds(kg + (off + k_chunk(r, lane & 15)),
+        const uint32_t off = (uint32_t)r * row_bytes;
+        __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
                                          (lds_void*)(ks + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vg + (off + v_chunk(r, lane & 15)),
+        __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
                                          (lds_void*)(ks + kTileBytes + i * 1024), 16, 0, 0);
       }
     };

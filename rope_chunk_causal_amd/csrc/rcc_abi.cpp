@@ -41,6 +41,42 @@ rcc_status check_cfg(const rcc_rope3d_cfg* c) {
   return RCC_OK;
 }
 
+int64_t table_floats(const rcc_rope3d_cfg& c) {
+  return (int64_t)c.max_t * c.d_t + (int64_t)c.max_h * c.d_h + (int64_t)c.max_w * c.d_w;
+}
+
+// FNV-1a over the descriptor's fields (not its padding bytes): a descriptor
+// whose cfg, buffer or length changed after init no longer matches its seal.
+uint64_t seal_of(const rcc_rope3d_tables& t) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  auto mix = [&h](const void* p, size_t n) {
+    const unsigned char* b = static_cast<const unsigned char*>(p);
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 0x100000001b3ull;
+  };
+  const rcc_rope3d_cfg& c = t.cfg;
+  mix(&c.d_t, 4); mix(&c.d_h, 4); mix(&c.d_w, 4); mix(&c.theta, 8);
+  mix(&c.max_t, 4); mix(&c.max_h, 4); mix(&c.max_w, 4);
+  const uintptr_t data = (uintptr_t)t.data;
+  mix(&data, sizeof(data));
+  mix(&t.floats, 8);
+  return h ^ 0x52434354424c5345ull;
+}
+
+// A descriptor is usable only as rcc_rope3d_tables_init sealed it; its
+// buffer then holds the layout of its cfg.
+rcc_status check_tables(const rcc_rope3d_tables* t) {
+  if (!t) return fail(RCC_ERR_NULL, "tables is NULL");
+  if (t->seal != seal_of(*t))
+    return fail(RCC_ERR_SHAPE,
+                "tables descriptor not made by rcc_rope3d_tables_init, or changed since");
+  rcc_status st = check_cfg(&t->cfg);
+  if (st != RCC_OK) return st;
+  if (!t->data || t->floats < table_floats(t->cfg))
+    return fail(RCC_ERR_SHAPE, "tables buffer of %lld floats, the cfg needs %lld",
+                (long long)t->floats, (long long)table_floats(t->cfg));
+  return RCC_OK;
+}
+
 // Grid + token range checks shared by positions and apply_append.
 rcc_status check_grid(const rcc_grid* g, int64_t n_tokens, rcc::GridArgs* out) {
   if (!g) return fail(RCC_ERR_NULL, "grid is NULL");
@@ -129,14 +165,16 @@ rcc_status check_cache_rows(const rcc_grid* grid, const rcc::GridArgs& g, int64_
   return RCC_OK;
 }
 
-rcc_status rope_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+rcc_status rope_append(const rcc_rope3d_tables* tables, const rcc_grid* grid,
                        const rcc_ring* ring, bool use_ring, rcc_dtype in_dtype,
                        rcc_dtype out_dtype, int32_t batch, int64_t n_tokens, int32_t n_heads,
                        const void* q, const void* k, const void* v, void* q_out,
                        void* k_cache, void* v_cache, int64_t cache_tokens,
                        hipStream_t stream) {
-  rcc_status st = check_cfg(cfg);
+  rcc_status st = check_tables(tables);
   if (st != RCC_OK) return st;
+  const rcc_rope3d_cfg* cfg = &tables->cfg;
+  const float* tables_dev = tables->data;
   rcc::GridArgs g;
   st = check_grid(grid, n_tokens, &g);
   if (st != RCC_OK) return st;
@@ -153,9 +191,9 @@ rcc_status rope_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const
   if ((st = check_tables_cover(cfg, grid)) != RCC_OK) return st;
   if ((st = check_cache_rows(grid, g, n_tokens, ring_rows, cache_tokens)) != RCC_OK) return st;
   if (n_tokens == 0) return RCC_OK;
-  if (!tables_dev || !q || !k || !v || !q_out || !k_cache || !v_cache)
+  if (!q || !k || !v || !q_out || !k_cache || !v_cache)
     return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
-  if (!aligned16(tables_dev) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) ||
       !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (q_out == (const void*)q && in_dtype != out_dtype)
@@ -184,13 +222,15 @@ rcc_status rope_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const
                   "rope3d_apply_append launch");
 }
 
-rcc_status qkv_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+rcc_status qkv_append(const rcc_rope3d_tables* tables, const rcc_grid* grid,
                       const rcc_ring* ring, bool use_ring, int32_t batch, int64_t n_tokens,
                       int32_t n_heads, int32_t model_dim, const void* x, const void* w_qkv,
                       const float* bias, void* q_out, void* k_cache, void* v_cache,
                       int64_t cache_tokens, hipStream_t stream) {
-  rcc_status st = check_cfg(cfg);
+  rcc_status st = check_tables(tables);
   if (st != RCC_OK) return st;
+  const rcc_rope3d_cfg* cfg = &tables->cfg;
+  const float* tables_dev = tables->data;
   rcc::GridArgs g;
   st = check_grid(grid, n_tokens, &g);
   if (st != RCC_OK) return st;
@@ -211,9 +251,9 @@ rcc_status qkv_append(const rcc_rope3d_cfg* cfg, const float* tables_dev, const 
   if ((st = check_tables_cover(cfg, grid)) != RCC_OK) return st;
   if ((st = check_cache_rows(grid, g, n_tokens, ring_rows, cache_tokens)) != RCC_OK) return st;
   if (n_tokens == 0) return RCC_OK;
-  if (!tables_dev || !x || !w_qkv || !q_out || !k_cache || !v_cache)
+  if (!x || !w_qkv || !q_out || !k_cache || !v_cache)
     return fail(RCC_ERR_NULL, "a tensor pointer is NULL");
-  if (!aligned16(tables_dev) || !aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) ||
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) ||
       !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)bias & 3u))
     return fail(RCC_ERR_ALIGN, "tensor pointers must be 16-byte aligned (bias 4-byte)");
 
@@ -261,17 +301,32 @@ const char* rcc_last_error(void) { return g_last_error; }
 
 int64_t rcc_rope3d_tables_floats(const rcc_rope3d_cfg* cfg) {
   if (check_cfg(cfg) != RCC_OK) return -1;
-  return (int64_t)cfg->max_t * cfg->d_t + (int64_t)cfg->max_h * cfg->d_h +
-         (int64_t)cfg->max_w * cfg->d_w;
+  return table_floats(*cfg);
 }
 
-rcc_status rcc_rope3d_tables(const rcc_rope3d_cfg* cfg, float* tables_dev,
-                             hipStream_t stream) {
+rcc_status rcc_rope3d_tables_init(const rcc_rope3d_cfg* cfg, float* buf_dev, int64_t buf_floats,
+                                  rcc_rope3d_tables* out) {
+  if (!out) return fail(RCC_ERR_NULL, "out is NULL");
+  memset(out, 0, sizeof(*out));
   rcc_status st = check_cfg(cfg);
   if (st != RCC_OK) return st;
-  if (!tables_dev) return fail(RCC_ERR_NULL, "tables_dev is NULL");
-  if (!aligned16(tables_dev)) return fail(RCC_ERR_ALIGN, "tables_dev not 16-byte aligned");
-  return from_hip(rcc::launch_rope3d_tables(*cfg, tables_dev, stream), "rope3d_tables launch");
+  if (!buf_dev) return fail(RCC_ERR_NULL, "buf_dev is NULL");
+  if (!aligned16(buf_dev)) return fail(RCC_ERR_ALIGN, "buf_dev not 16-byte aligned");
+  if (buf_floats < table_floats(*cfg))
+    return fail(RCC_ERR_SHAPE, "buffer of %lld floats, the cfg needs %lld",
+                (long long)buf_floats, (long long)table_floats(*cfg));
+  out->cfg = *cfg;
+  out->data = buf_dev;
+  out->floats = buf_floats;
+  out->seal = seal_of(*out);
+  return RCC_OK;
+}
+
+rcc_status rcc_rope3d_tables_build(const rcc_rope3d_tables* tables, hipStream_t stream) {
+  rcc_status st = check_tables(tables);
+  if (st != RCC_OK) return st;
+  return from_hip(rcc::launch_rope3d_tables(tables->cfg, tables->data, stream),
+                  "rope3d_tables launch");
 }
 
 rcc_status rcc_rope3d_positions(const rcc_grid* grid, int64_t n_tokens, int32_t* thw_dev,
@@ -309,44 +364,44 @@ int64_t rcc_ring_held_tokens(const rcc_grid* grid, const rcc_ring* ring) {
 }
 
 rcc_status rcc_rope3d_apply_append(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     rcc_dtype in_dtype, rcc_dtype out_dtype,
     int32_t batch, int64_t n_tokens, int32_t n_heads,
     const void* q, const void* k, const void* v,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
     hipStream_t stream) {
-  return rope_append(cfg, tables_dev, grid, nullptr, false, in_dtype, out_dtype, batch,
+  return rope_append(tables, grid, nullptr, false, in_dtype, out_dtype, batch,
                      n_tokens, n_heads, q, k, v, q_out, k_cache, v_cache, cache_tokens, stream);
 }
 
 rcc_status rcc_rope3d_apply_append_ring(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     const rcc_ring* ring, rcc_dtype in_dtype, rcc_dtype out_dtype,
     int32_t batch, int64_t n_tokens, int32_t n_heads,
     const void* q, const void* k, const void* v,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
     hipStream_t stream) {
-  return rope_append(cfg, tables_dev, grid, ring, true, in_dtype, out_dtype, batch,
+  return rope_append(tables, grid, ring, true, in_dtype, out_dtype, batch,
                      n_tokens, n_heads, q, k, v, q_out, k_cache, v_cache, cache_tokens, stream);
 }
 
 rcc_status rcc_qkv_rope_append(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     int32_t batch, int64_t n_tokens, int32_t n_heads, int32_t model_dim,
     const void* x, const void* w_qkv, const float* bias,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
     hipStream_t stream) {
-  return qkv_append(cfg, tables_dev, grid, nullptr, false, batch, n_tokens, n_heads, model_dim,
+  return qkv_append(tables, grid, nullptr, false, batch, n_tokens, n_heads, model_dim,
                     x, w_qkv, bias, q_out, k_cache, v_cache, cache_tokens, stream);
 }
 
 rcc_status rcc_qkv_rope_append_ring(
-    const rcc_rope3d_cfg* cfg, const float* tables_dev, const rcc_grid* grid,
+    const rcc_rope3d_tables* tables, const rcc_grid* grid,
     const rcc_ring* ring, int32_t batch, int64_t n_tokens, int32_t n_heads,
     int32_t model_dim, const void* x, const void* w_qkv, const float* bias,
     void* q_out, void* k_cache, void* v_cache, int64_t cache_tokens,
     hipStream_t stream) {
-  return qkv_append(cfg, tables_dev, grid, ring, true, batch, n_tokens, n_heads, model_dim,
+  return qkv_append(tables, grid, ring, true, batch, n_tokens, n_heads, model_dim,
                     x, w_qkv, bias, q_out, k_cache, v_cache, cache_tokens, stream);
 }
 
@@ -446,9 +501,6 @@ rcc_status rcc_block_sparse_attn(
   if (kv_tokens > cache_tokens)
     return fail(RCC_ERR_RANGE, "kv_tokens %lld > cache_tokens %lld", (long long)kv_tokens,
                 (long long)cache_tokens);
-  // K/V loads use 32-bit byte offsets inside one batch entry's cache.
-  if (cache_tokens * n_heads * 256 > (int64_t)UINT32_MAX)
-    return fail(RCC_ERR_SHAPE, "a batch entry's cache must be smaller than 4 GiB");
   const int64_t n_qb = (q_tokens + block_tokens - 1) / block_tokens;
   if (q_tokens > kI32Max || n_qb * n_heads * batch > kI32Max)
     return fail(RCC_ERR_SHAPE, "sizes must be < 2^31");

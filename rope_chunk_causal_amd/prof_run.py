@@ -61,7 +61,7 @@ def rope(name: str, reps: int, gen) -> None:
     vc = torch.empty_like(kc)
     g = rcc.grid(wl.frames, wl.height, wl.width, s, off)
     for _ in range(reps):
-        rcc.rope3d_apply_append(cfg, tables, g, q, k, v, qo, kc, vc)
+        rcc.rope3d_apply_append(tables, g, q, k, v, qo, kc, vc)
 
 
 def qkv(name: str, reps: int, gen) -> None:
@@ -84,7 +84,7 @@ def qkv(name: str, reps: int, gen) -> None:
     vc = torch.empty_like(kc)
     g = rcc.grid(wl.frames, wl.height, wl.width, s, off)
     for _ in range(reps):
-        rcc.qkv_rope_append(cfg, tables, g, x, w, None, qo, kc, vc)
+        rcc.qkv_rope_append(tables, g, x, w, None, qo, kc, vc)
 
 
 def ring_1min(reps: int, gen) -> None:
@@ -106,7 +106,7 @@ def ring_1min(reps: int, gen) -> None:
             for _ in range(wl.steps):
                 q, k, v = sets[i % 4]
                 i += 1
-                rcc.rope3d_apply_append_ring(cfg, tables, g, ring, q, k, v, qo, kc, vc)
+                rcc.rope3d_apply_append_ring(tables, g, ring, q, k, v, qo, kc, vc)
                 rcc.chunk_causal_attn_ring(g, ring, qo, kc, vc, out, 1 / math.sqrt(D))
 
 

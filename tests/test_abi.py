@@ -51,6 +51,15 @@ def _gpu_present():
 FAKE = 1 << 40
 
 
+def _sealed(cfg, buf=FAKE, floats=None):
+    """A tables descriptor from rcc_rope3d_tables_init (host only) over a fake
+    buffer of exactly the cfg's size; zeroed if init rejects the cfg."""
+    desc = rcc.rcc_rope3d_tables()
+    n = rcc.lib().rcc_rope3d_tables_floats(ctypes.byref(cfg)) if floats is None else floats
+    rcc.lib().rcc_rope3d_tables_init(ctypes.byref(cfg), buf, n, ctypes.byref(desc))
+    return desc
+
+
 @pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
 @pytest.mark.parametrize("kw,status", [
     (dict(in_dtype=7), rcc.RCC_ERR_DTYPE),
@@ -99,7 +108,7 @@ def test_apply_host_checks(kw, status):
              q=FAKE, k=FAKE, v=FAKE, q_out=FAKE + 4096, kc=FAKE, vc=FAKE, cache=96)
     a.update(kw)
     st = rcc.lib().rcc_rope3d_apply_append(
-        ctypes.byref(a["cfg"]), FAKE, ctypes.byref(a["grid"]), a["in_dtype"], a["out_dtype"],
+        ctypes.byref(_sealed(a["cfg"])), ctypes.byref(a["grid"]), a["in_dtype"], a["out_dtype"],
         a["batch"], a["n"], a["nh"], a["q"], a["k"], a["v"], a["q_out"], a["kc"], a["vc"],
         a["cache"], None)
     assert st == status, rcc.lib().rcc_last_error()
@@ -112,10 +121,65 @@ def test_positions_and_tables_host_checks():
     assert L.rcc_rope3d_positions(ctypes.byref(g), 3, FAKE, None) == rcc.RCC_ERR_RANGE
     assert L.rcc_rope3d_positions(ctypes.byref(g), 2, 0, None) == rcc.RCC_ERR_NULL
     assert L.rcc_rope3d_positions(ctypes.byref(g), 0, 0, None) == rcc.RCC_OK
+    desc = rcc.rcc_rope3d_tables()
     bad = rcc.rope_cfg(8, 8, 8, 16, 4, 0)
-    assert L.rcc_rope3d_tables(ctypes.byref(bad), FAKE, None) == rcc.RCC_ERR_SHAPE
+    assert L.rcc_rope3d_tables_init(ctypes.byref(bad), FAKE, 1 << 20, ctypes.byref(desc)) == \
+        rcc.RCC_ERR_SHAPE
     good = rcc.rope_cfg(8, 8, 8, 16, 4, 4)
-    assert L.rcc_rope3d_tables(ctypes.byref(good), FAKE + 4, None) == rcc.RCC_ERR_ALIGN
+    assert L.rcc_rope3d_tables_init(ctypes.byref(good), FAKE + 4, 1 << 20, ctypes.byref(desc)) == \
+        rcc.RCC_ERR_ALIGN
+    assert L.rcc_rope3d_tables_init(ctypes.byref(good), 0, 1 << 20, ctypes.byref(desc)) == \
+        rcc.RCC_ERR_NULL
+    assert L.rcc_rope3d_tables_init(ctypes.byref(good), FAKE, 1 << 20, None) == rcc.RCC_ERR_NULL
+    assert L.rcc_rope3d_tables_build(None, None) == rcc.RCC_ERR_NULL
+
+
+@pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
+def test_tables_descriptor_binds_its_cfg_to_its_buffer():
+    """A descriptor is made only by init, for a buffer of at least the cfg's
+    size; a call given a descriptor whose cfg, buffer or length changed
+    afterwards, or one init never sealed, fails its host check and launches
+    nothing (no GPU here: any launch would fail with RCC_ERR_HIP instead)."""
+    L = rcc.lib()
+    cfg = rcc.rope_cfg(8, 8, 8, 16, 4, 4)
+    n = L.rcc_rope3d_tables_floats(ctypes.byref(cfg))
+    assert n == 16 * 8 + 4 * 8 + 4 * 8
+    desc = rcc.rcc_rope3d_tables()
+    # a buffer one float short is refused, and the descriptor left unsealed
+    assert L.rcc_rope3d_tables_init(ctypes.byref(cfg), FAKE, n - 1, ctypes.byref(desc)) == \
+        rcc.RCC_ERR_SHAPE
+    assert desc.seal == 0 and desc.data is None
+
+    def apply(d, grid=rcc.grid(2, 4, 4, 4, 0), cache=96):
+        return L.rcc_rope3d_apply_append(ctypes.byref(d), ctypes.byref(grid), rcc.RCC_F32,
+                                         rcc.RCC_F32, 1, 32, 2, FAKE, FAKE, FAKE, FAKE + 4096,
+                                         FAKE, FAKE, cache, None)
+
+    def qkv(d):
+        return L.rcc_qkv_rope_append(ctypes.byref(d), ctypes.byref(rcc.grid(2, 4, 4, 4, 0)), 1,
+                                     32, 2, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, 96, None)
+
+    assert apply(desc) == rcc.RCC_ERR_SHAPE            # never sealed
+    assert L.rcc_rope3d_tables_build(ctypes.byref(desc), None) == rcc.RCC_ERR_SHAPE
+    assert L.rcc_rope3d_tables_init(ctypes.byref(cfg), FAKE, n, ctypes.byref(desc)) == rcc.RCC_OK
+    assert desc.floats == n and desc.data == FAKE and desc.cfg.max_t == 16
+    # the sealed descriptor passes: these fail later, on the grid and cache checks
+    assert apply(desc, grid=rcc.grid(2, 4, 4, 15, 0)) == rcc.RCC_ERR_RANGE   # s + F > max_t
+    assert apply(desc, cache=95) == rcc.RCC_ERR_RANGE
+    for field, value in (("max_t", 1024), ("max_h", 64), ("d_t", 16), ("theta", 500.0)):
+        changed = rcc.rcc_rope3d_tables.from_buffer_copy(desc)
+        setattr(changed.cfg, field, value)
+        assert apply(changed) == rcc.RCC_ERR_SHAPE, field
+        assert qkv(changed) == rcc.RCC_ERR_SHAPE, field
+        assert L.rcc_rope3d_tables_build(ctypes.byref(changed), None) == rcc.RCC_ERR_SHAPE
+    for field, value in (("floats", n - 1), ("floats", 1 << 30), ("data", FAKE + 4096)):
+        changed = rcc.rcc_rope3d_tables.from_buffer_copy(desc)
+        setattr(changed, field, value)
+        assert apply(changed) == rcc.RCC_ERR_SHAPE, field
+    # a larger buffer than needed is fine
+    assert L.rcc_rope3d_tables_init(ctypes.byref(cfg), FAKE, n + 100, ctypes.byref(desc)) == \
+        rcc.RCC_OK
+    assert apply(desc, cache=95) == rcc.RCC_ERR_RANGE
 
 
 @pytest.mark.skipif(_gpu_present(), reason="host-check cases use fake pointers; CPU only")
@@ -144,7 +208,7 @@ def test_qkv_host_checks(kw, status):
         a["cfg"] = rcc.rope_cfg(16, 8, 8, 16, 1024, 1024)
         a["cache"] = a["n"]
     st = rcc.lib().rcc_qkv_rope_append(
-        ctypes.byref(a["cfg"]), FAKE, ctypes.byref(a["grid"]), a["batch"], a["n"], a["nh"],
+        ctypes.byref(_sealed(a["cfg"])), ctypes.byref(a["grid"]), a["batch"], a["n"], a["nh"],
         a["model_dim"], a["x"], a["w"], a["bias"], a["q_out"], a["kc"], a["vc"], a["cache"],
         None)
     assert st == status, rcc.lib().rcc_last_error()
@@ -194,7 +258,7 @@ def test_apply_ring_host_checks(kw, status):
     L = rcc.lib()
     ring = ctypes.byref(a["ring"]) if a["ring"] is not None else None
     st = L.rcc_rope3d_apply_append_ring(
-        ctypes.byref(a["cfg"]), FAKE, ctypes.byref(a["grid"]), ring, rcc.RCC_F32,
+        ctypes.byref(_sealed(a["cfg"])), ctypes.byref(a["grid"]), ring, rcc.RCC_F32,
         rcc.RCC_F32, 1, 32, 2, a["q"], a["k"], a["v"], FAKE + 4096, FAKE, FAKE, a["cache"],
         None)
     assert st == status, L.rcc_last_error()
@@ -202,7 +266,7 @@ def test_apply_ring_host_checks(kw, status):
         # the fused projection applies the same ring rules (D = 32 here)
         cfg = rcc.rope_cfg(16, 8, 8, 16, 4, 4)
         st = L.rcc_qkv_rope_append_ring(
-            ctypes.byref(cfg), FAKE, ctypes.byref(a["grid"]), ring, 1, 32, 2, 64, FAKE, FAKE,
+            ctypes.byref(_sealed(cfg)), ctypes.byref(a["grid"]), ring, 1, 32, 2, 64, FAKE, FAKE,
             None, FAKE, FAKE, FAKE, a["cache"], None)
         assert st == status, L.rcc_last_error()
 
@@ -239,7 +303,6 @@ def test_ring_positions_and_attention_host_checks():
     (dict(n_p=600, n_l=425), rcc.RCC_ERR_SHAPE),             # more than 1024 entries
     (dict(kv=32768 * 32 + 32, cache=1 << 21, block=32), rcc.RCC_ERR_SHAPE),  # > 32768 blocks
     (dict(kv=1025), rcc.RCC_ERR_RANGE),                      # beyond the cache
-    (dict(cache=1 << 22, nh=8), rcc.RCC_ERR_SHAPE),          # a batch entry's cache >= 4 GiB
     (dict(scale=0.0), rcc.RCC_ERR_SHAPE),
     (dict(n_l=-1), rcc.RCC_ERR_SHAPE),
     (dict(persist=0), rcc.RCC_ERR_NULL),
@@ -265,15 +328,22 @@ C_PROGRAM = r"""
 #include "rcc.h"
 
 int main(void) {
-  rcc_rope3d_cfg cfg = {44, 42, 42, 1024, 64, 128, 10000.0};
+  rcc_rope3d_cfg cfg = {44, 42, 42, 10000.0, 1024, 64, 128};
   rcc_grid g = {3, 30, 52, 6, 0};
   rcc_ring ring = {0, 21, 0, 0};
+  rcc_rope3d_tables tab;
   long long floats = (long long)rcc_rope3d_tables_floats(&cfg);
   long long held = (long long)rcc_ring_held_tokens(&g, &ring);
   rcc_status st = rcc_chunk_causal_attn(RCC_BF16, RCC_BF16, 1, 12, 128, 4680, 9360, 14040,
                                         4680, 0.0883883f, NULL, NULL, NULL, 14040, NULL, NULL);
-  printf("%lld %lld %s %d\n", floats, held, rcc_status_string(st),
-         (int)(strlen(rcc_last_error()) > 0));
+  /* a descriptor over a fake (never touched) device address, then changed */
+  rcc_status init = rcc_rope3d_tables_init(&cfg, (float*)(size_t)0x10000000000ull, floats, &tab);
+  tab.cfg.max_t = 4096;
+  rcc_status changed = rcc_rope3d_apply_append(&tab, &g, RCC_BF16, RCC_BF16, 1, 4680, 12,
+                                               NULL, NULL, NULL, NULL, NULL, NULL, 14040, NULL);
+  printf("%lld %lld %s %d %s %s\n", floats, held, rcc_status_string(st),
+         (int)(strlen(rcc_last_error()) > 0), rcc_status_string(init),
+         rcc_status_string(changed));
   return 0;
 }
 """
@@ -281,7 +351,8 @@ int main(void) {
 
 def test_header_compiles_as_c99_and_links():
     """A plain C99 program includes rcc.h, links librcc.so and makes host-only
-    calls (sizes, ring rows, an argument error): the boundary needs no C++."""
+    calls (sizes, ring rows, an argument error, a tables descriptor rejected
+    after its cfg changed): the boundary needs no C++."""
     import shutil
     import subprocess
     gcc = shutil.which("gcc")
@@ -301,7 +372,8 @@ def test_header_compiles_as_c99_and_links():
     assert "rcc.h" not in r.stderr, r.stderr       # no warnings from our header
     out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0, out.stderr
-    floats, held, status, has_detail = out.stdout.split()
+    floats, held, status, has_detail, init, changed = out.stdout.split()
     assert int(floats) == 2 * (1024 * 22 + 64 * 21 + 128 * 21)
     assert int(held) == 9 * 1560
     assert status == "RCC_ERR_NULL" and has_detail == "1"
+    assert init == "RCC_OK" and changed == "RCC_ERR_SHAPE"

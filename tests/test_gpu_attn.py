@@ -82,30 +82,6 @@ def test_ragged_and_masked_shapes(b, lq, nh, d, cap, q_pos, kv, C, in_dt, out_dt
     check_attn(got, ref, f"{(b, lq, nh, d, q_pos, kv, C)}")
 
 
-def test_cache_over_4gib_per_batch_entry():
-    """A bf16 head_dim-128 cache of 2^24 + 32 rows per batch entry (4.3 GB for
-    K alone) is past the fast kernel's 32-bit in-entry offsets, so the call
-    takes the generic kernel; batch entry 1 then starts 4.3 GB into the
-    cache.  Only the first kv rows of each entry are written and read."""
-    t = torch()
-    b, lq, nh, d, cap, q_pos, kv, C = 2, 100, 1, 128, (1 << 24) + 32, 200, 300, 100
-    q = synth.normal((b, lq, nh, d), 501, "bf16")
-    k = synth.normal((b, kv, nh, d), 502, "bf16")
-    v = synth.normal((b, kv, nh, d), 503, "bf16")
-    say("attn cache > 4 GiB per entry", cap)
-    kc = t.empty((b, cap, nh, d), dtype=t.bfloat16, device="cuda")
-    vc = t.empty((b, cap, nh, d), dtype=t.bfloat16, device="cuda")
-    kc[:, :kv] = to_dev(k, "bf16")
-    vc[:, :kv] = to_dev(v, "bf16")
-    out = t.full((b, lq, nh, d), float("nan"), dtype=t.bfloat16, device="cuda")
-    rcc.chunk_causal_attn(to_dev(q, "bf16"), kc, vc, out, q_pos, kv, C, 1.0 / math.sqrt(d))
-    t.cuda.synchronize()
-    ref = A.chunk_causal_attention(synth.to_f64(q, "bf16"), synth.to_f64(k, "bf16"),
-                                   synth.to_f64(v, "bf16"), q_pos, kv, C, 1.0 / math.sqrt(d))
-    check_attn(to_host_f64(out), ref, "cache > 4 GiB")
-    del kc, vc
-
-
 def _sample_rows(lq, n, seed):
     r = np.random.default_rng(seed).choice(lq, size=min(n, lq), replace=False)
     edges = [0, 1, 31, 32, 127, 128, lq - 129, lq - 128, lq - 2, lq - 1]

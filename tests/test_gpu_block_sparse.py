@@ -176,7 +176,7 @@ def test_block_sparse_over_a_rolling_ring(bh, bw):
         dq, dk, dv = (to_dev(x, "bf16") for x in host)
         qo = t.empty_like(dq)
         say("ring + sparse: write chunk", c)
-        rcc.rope3d_apply_append_ring(cfg, tables, rcc.grid(F, H, W, s, 0), r, dq, dk, dv, qo,
+        rcc.rope3d_apply_append_ring(tables, rcc.grid(F, H, W, s, 0), r, dq, dk, dv, qo,
                                      kr, vr)
         q, k, v = (synth.to_f64(x, "bf16") for x in host)
         oq = G.rope3d_apply_append(q, k, v, okr, ovr, otab, F, H, W, s, 0, sink, window, bh, bw)

@@ -33,7 +33,7 @@ def test_graph_replays_match_eager_bitwise():
     scale = 1.0 / math.sqrt(D)
 
     def step(kc, vc, qo, out):
-        rcc.rope3d_apply_append(cfg, tables, g, q, k, v, qo, kc, vc)
+        rcc.rope3d_apply_append(tables, g, q, k, v, qo, kc, vc)
         rcc.chunk_causal_attn(qo, kc, vc, out, s * hw, cap, L, scale)
 
     say("graph: eager reference")

@@ -39,7 +39,7 @@ def _run(B, n, nh, dims, K, F, H, W, s, off, mx, bias, seed, sample=None):
     qo = t.full((B, n, nh, D), float("nan"), dtype=t.bfloat16, device="cuda")
     kc = t.full((B, cap, nh, D), SENTINEL, dtype=t.bfloat16, device="cuda")
     vc = t.full_like(kc, SENTINEL)
-    rcc.qkv_rope_append(cfg, tables, rcc.grid(F, H, W, s, off), x, w, bdev, qo, kc, vc)
+    rcc.qkv_rope_append(tables, rcc.grid(F, H, W, s, off), x, w, bdev, qo, kc, vc)
     t.cuda.synchronize()
 
     tok = np.arange(n) if sample is None else sample
@@ -119,7 +119,7 @@ def test_zero_tokens_is_a_no_op():
     qo = t.zeros((1, 0, 2, 32), dtype=t.bfloat16, device="cuda")
     kc = t.full((1, 64, 2, 32), SENTINEL, dtype=t.bfloat16, device="cuda")
     vc = t.full_like(kc, SENTINEL)
-    rcc.qkv_rope_append(cfg, tables, rcc.grid(2, 4, 4, 0, 0), x, w, None, qo, kc, vc)
+    rcc.qkv_rope_append(tables, rcc.grid(2, 4, 4, 0, 0), x, w, None, qo, kc, vc)
     t.cuda.synchronize()
     assert bool((kc == SENTINEL).all()) and bool((vc == SENTINEL).all())
 
@@ -133,8 +133,8 @@ def test_errors_reported_without_launch():
     qo = t.zeros((1, 8, 2, 32), dtype=t.bfloat16, device="cuda")
     kc = t.zeros((1, 64, 2, 32), dtype=t.bfloat16, device="cuda")
     with pytest.raises(rcc.RccError) as e:
-        rcc.qkv_rope_append(cfg, tables, rcc.grid(2, 4, 4, 0, 0), x, w, None, qo, kc, kc.clone())
+        rcc.qkv_rope_append(tables, rcc.grid(2, 4, 4, 0, 0), x, w, None, qo, kc, kc.clone())
     assert e.value.status == rcc.RCC_ERR_SHAPE
     with pytest.raises(TypeError):
-        rcc.qkv_rope_append(cfg, tables, rcc.grid(2, 4, 4, 0, 0), x.float(), w, None, qo, kc,
+        rcc.qkv_rope_append(tables, rcc.grid(2, 4, 4, 0, 0), x.float(), w, None, qo, kc,
                             kc.clone())

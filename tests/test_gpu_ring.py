@@ -67,7 +67,7 @@ def test_ring_rollout_tiny_fp32_every_element():
             qo, out = t.empty_like(dq), t.full_like(dq, float("nan"))
             g, r = rcc.grid(F, H, W, s, 0), rcc.ring(sink, window)
             say("ring tiny fp32 chunk", c, "step", step)
-            rcc.rope3d_apply_append_ring(cfg, tables, g, r, dq, dk, dv, qo, kr, vr)
+            rcc.rope3d_apply_append_ring(tables, g, r, dq, dk, dv, qo, kr, vr)
             rcc.chunk_causal_attn_ring(g, r, qo, kr, vr, out, scale)
             t.cuda.synchronize()
             q, k, v = (x.astype(np.float64) for x in host)
@@ -101,7 +101,7 @@ def test_ring_rollout_bf16_d128_small():
         qo, out = t.empty_like(dq), t.full_like(dq, float("nan"))
         g, r = rcc.grid(F, H, W, s, 0), rcc.ring(sink, window)
         say("ring bf16 d128 chunk", c)
-        rcc.rope3d_apply_append_ring(cfg, tables, g, r, dq, dk, dv, qo, kr, vr)
+        rcc.rope3d_apply_append_ring(tables, g, r, dq, dk, dv, qo, kr, vr)
         rcc.chunk_causal_attn_ring(g, r, qo, kr, vr, out, scale)
         t.cuda.synchronize()
         q, k, v = (synth.to_f64(x, "bf16") for x in host)
@@ -142,7 +142,7 @@ def test_480p_long_rollout_ring_sampled(name, sink, window, last):
         qo = t.empty_like(dq)
         g = rcc.grid(F, wl.height, wl.width, s, 0)
         say(name, "ring write s", s)
-        rcc.rope3d_apply_append_ring(cfg, tables, g, r, dq, dk, dv, qo, kr, vr)
+        rcc.rope3d_apply_append_ring(tables, g, r, dq, dk, dv, qo, kr, vr)
         q, k, v = (synth.to_f64(x, "bf16") for x in host)
         oq = G.rope3d_apply_append(q, k, v, okr, ovr, otab, F, wl.height, wl.width, s, 0,
                                    sink, window)
@@ -185,7 +185,7 @@ def test_qkv_ring_write(bh, bw):
             xb = synth.normal((1, n, K), 40 + 10 * c + off, "bf16")
             qo = t.empty((1, n, nh, D), dtype=t.bfloat16, device="cuda")
             say("qkv ring chunk", c, "slice", off, n)
-            rcc.qkv_rope_append_ring(cfg, tables, rcc.grid(F, H, W, s, off),
+            rcc.qkv_rope_append_ring(tables, rcc.grid(F, H, W, s, off),
                                      rcc.ring(sink, window, bh, bw), to_dev(xb, "bf16"), w, bdev,
                                      qo, kr, vr)
             t.cuda.synchronize()
@@ -216,8 +216,8 @@ def test_ring_without_eviction_matches_the_plain_cache_bitwise():
         o1, o2 = t.empty_like(dq), t.empty_like(dq)
         g = rcc.grid(F, wl.height, wl.width, s, 0)
         say("ring vs plain s", s)
-        rcc.rope3d_apply_append(cfg, tables, g, dq, dk, dv, q1, caches[0], caches[1])
-        rcc.rope3d_apply_append_ring(cfg, tables, g, r, dq, dk, dv, q2, caches[2], caches[3])
+        rcc.rope3d_apply_append(tables, g, dq, dk, dv, q1, caches[0], caches[1])
+        rcc.rope3d_apply_append_ring(tables, g, r, dq, dk, dv, q2, caches[2], caches[3])
         rcc.chunk_causal_attn(q1, caches[0], caches[1], o1, s * hw, (s + F) * hw, L,
                               1.0 / math.sqrt(D))
         rcc.chunk_causal_attn_ring(g, r, q2, caches[2], caches[3], o2, 1.0 / math.sqrt(D))
@@ -236,11 +236,11 @@ def test_ring_errors_reported_without_launch():
     q = t.zeros((1, 32, 2, 32), dtype=t.bfloat16, device="cuda")
     kr = t.zeros((1, 48, 2, 32), dtype=t.bfloat16, device="cuda")
     with pytest.raises(rcc.RccError) as e:      # window smaller than the chunk
-        rcc.rope3d_apply_append_ring(cfg, tables, rcc.grid(2, 4, 4, 0), rcc.ring(0, 1),
+        rcc.rope3d_apply_append_ring(tables, rcc.grid(2, 4, 4, 0), rcc.ring(0, 1),
                                      q, q, q, q.clone(), kr, kr.clone())
     assert e.value.status == rcc.RCC_ERR_SHAPE
     with pytest.raises(rcc.RccError) as e:      # ring of 4 frames needs 64 rows
-        rcc.rope3d_apply_append_ring(cfg, tables, rcc.grid(2, 4, 4, 8), rcc.ring(1, 3),
+        rcc.rope3d_apply_append_ring(tables, rcc.grid(2, 4, 4, 8), rcc.ring(1, 3),
                                      q, q, q, q.clone(), kr, kr.clone())
     assert e.value.status == rcc.RCC_ERR_RANGE
     assert bool((kr == 0).all())

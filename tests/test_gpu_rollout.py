@@ -52,7 +52,7 @@ def test_480p_rollout_every_step():
             out = t.full_like(dq, float("nan"))
             kv = (s + wl.frames) * hw
             say("rollout chunk", c, "step", step, "kv", kv)
-            rcc.rope3d_apply_append(cfg, tables, rcc.grid(wl.frames, wl.height, wl.width, s, 0),
+            rcc.rope3d_apply_append(tables, rcc.grid(wl.frames, wl.height, wl.width, s, 0),
                                     dq, dk, dv, qo, kc, vc)
             rcc.chunk_causal_attn(qo, kc, vc, out, s * hw, kv, L, scale)
             t.cuda.synchronize()

@@ -38,7 +38,7 @@ def test_tables_match_oracle(dims, mx):
     say("tables", dims, mx)
     t = rcc.rope3d_tables(cfg)
     torch().cuda.synchronize()
-    got = t.cpu().double().numpy()
+    got = t.buf.cpu().double().numpy()
     ref = _flat_oracle_table(cfg)
     assert got.shape == ref.shape
     # fp64 cos/sin rounded once to fp32: within one fp32 rounding of the oracle
@@ -75,7 +75,7 @@ def _run_apply(wl, s, off, n, batch, in_dt, out_dt, seed, cap=None, poison=True)
     kc = t.full((batch, cap, wl.n_heads, wl.head_dim), 3.0, dtype=tdt, device="cuda")
     vc = t.full((batch, cap, wl.n_heads, wl.head_dim), -3.0, dtype=tdt, device="cuda")
     dq, dk, dv = to_dev(q, in_dt), to_dev(k, in_dt), to_dev(v, in_dt)
-    rcc.rope3d_apply_append(cfg, tables, rcc.grid(wl.frames, wl.height, wl.width, s, off),
+    rcc.rope3d_apply_append(tables, rcc.grid(wl.frames, wl.height, wl.width, s, off),
                             dq, dk, dv, qo, kc, vc)
     t.cuda.synchronize()
     return cfg, (q, k, v), (qo, kc, vc), cap
@@ -181,13 +181,13 @@ def test_sp_shards_bit_equal_unsharded_and_match_oracle():
                      t.zeros((1, cap, wl.n_heads, wl.head_dim), dtype=t.bfloat16, device="cuda"),
                      t.zeros((1, cap, wl.n_heads, wl.head_dim), dtype=t.bfloat16, device="cuda")])
     say("sp full")
-    rcc.rope3d_apply_append(cfg, tables, g_full, dq, dk, dv, *outs[0])
+    rcc.rope3d_apply_append(tables, g_full, dq, dk, dv, *outs[0])
     n = L // P
     for r in range(P):
         say("sp shard", r)
         sl = slice(r * n, (r + 1) * n)
         qo_r = t.empty((1, n, wl.n_heads, wl.head_dim), dtype=t.bfloat16, device="cuda")
-        rcc.rope3d_apply_append(cfg, tables, rcc.grid(wl.frames, wl.height, wl.width, s, r * n),
+        rcc.rope3d_apply_append(tables, rcc.grid(wl.frames, wl.height, wl.width, s, r * n),
                                 dq[:, sl].contiguous(), dk[:, sl].contiguous(),
                                 dv[:, sl].contiguous(), qo_r, outs[1][1], outs[1][2])
         outs[1][0][:, sl] = qo_r
@@ -245,7 +245,7 @@ def test_in_place_q_and_determinism():
         kc = t.zeros((1, cap, wl.n_heads, wl.head_dim), dtype=t.bfloat16, device="cuda")
         vc = t.zeros_like(kc)
         say("inplace", inplace)
-        rcc.rope3d_apply_append(cfg, tables, g, dq, dk, dv, qo, kc, vc)
+        rcc.rope3d_apply_append(tables, g, dq, dk, dv, qo, kc, vc)
         t.cuda.synchronize()
         res.append((qo.view(t.int16).cpu(), kc.view(t.int16).cpu()))
     for a in res[1:]:
@@ -259,7 +259,7 @@ def test_zero_tokens_is_a_no_op():
     tables = rcc.rope3d_tables(cfg)
     e = t.empty((1, 0, 2, 24), device="cuda")
     kc = t.full((1, 96, 2, 24), 5.0, device="cuda")
-    rcc.rope3d_apply_append(cfg, tables, rcc.grid(2, 4, 4, 2, 32), e, e, e, e, kc, kc.clone())
+    rcc.rope3d_apply_append(tables, rcc.grid(2, 4, 4, 2, 32), e, e, e, e, kc, kc.clone())
     t.cuda.synchronize()
     assert bool((kc == 5.0).all())
 
@@ -272,13 +272,13 @@ def test_errors_reported_without_launch():
     x = t.zeros((1, 32, 2, 24), device="cuda")
     kc = t.full((1, 64, 2, 24), 9.0, device="cuda")
     with pytest.raises(rcc.RccError) as e:   # s + F > max_t
-        rcc.rope3d_apply_append(cfg, tables, rcc.grid(2, 4, 4, 15, 0), x, x, x, x.clone(), kc, kc)
+        rcc.rope3d_apply_append(tables, rcc.grid(2, 4, 4, 15, 0), x, x, x, x.clone(), kc, kc)
     assert e.value.status == rcc.RCC_ERR_RANGE
     with pytest.raises(rcc.RccError) as e:   # cache too small for rows 64..95
-        rcc.rope3d_apply_append(cfg, tables, rcc.grid(2, 4, 4, 4, 0), x, x, x, x.clone(), kc, kc)
+        rcc.rope3d_apply_append(tables, rcc.grid(2, 4, 4, 4, 0), x, x, x, x.clone(), kc, kc)
     assert e.value.status == rcc.RCC_ERR_RANGE
     with pytest.raises(rcc.RccError) as e:   # Delta + n beyond the chunk
-        rcc.rope3d_apply_append(cfg, tables, rcc.grid(2, 4, 4, 0, 1), x, x, x, x.clone(), kc, kc)
+        rcc.rope3d_apply_append(tables, rcc.grid(2, 4, 4, 0, 1), x, x, x, x.clone(), kc, kc)
     assert e.value.status == rcc.RCC_ERR_RANGE
     t.cuda.synchronize()
     assert bool((kc == 9.0).all())
