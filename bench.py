@@ -272,6 +272,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows, wl, s, kv, scale)
+        result["cpu_oracle_other_workloads"] = cpu_oracle_workloads()
     print(json.dumps(result), flush=True)
 
 
@@ -567,52 +568,162 @@ def block_sparse(rcc, synth, randn, stream, dev):
     return out
 
 
+def _host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS threads numpy uses."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    return model, threads
+
+
+def _oracle_chunks(wl, name, starts, tabs, cache_tokens, n_heads=None):
+    """The oracle's cache after RoPE + append of the chunks at `starts` (seeded
+    q, k, v per chunk, as the tests draw them); returns (cache k, cache v,
+    rotated q of the last chunk, its positions)."""
+    import numpy as np
+    from oracle import rope3d as R
+    from rope_chunk_causal_amd import synth
+    nh = wl.n_heads if n_heads is None else n_heads
+    L, D = wl.chunk_tokens, wl.head_dim
+    kc = np.zeros((1, cache_tokens, nh, D))
+    vc = np.zeros((1, cache_tokens, nh, D))
+    q = pos = None
+    for s in starts:
+        q, k, v = (synth.to_f64(synth.normal((1, L, nh, D), synth.seed_for(name, s, 0, x),
+                                             "bf16"), "bf16") for x in ("q", "k", "v"))
+        pos = R.positions(wl.frames, wl.height, wl.width, s, 0, L)
+        q = R.rope3d_apply_append(q, k, v, kc, vc, tabs, wl.frames, wl.height, wl.width, s, 0)
+    return kc, vc, q, pos
+
+
 def cpu_baseline(rows_per_head, wl, s, kv, scale):
-    """The oracle (as it stands) timed on the host on a bounded sample of the step:
-    attention for `rows_per_head` query rows of every head, plus RoPE + append of
-    the same tokens.  Reported in the metric's unit (TFLOP/s of attention)."""
+    """The oracle (as it stands) timed on the host on the 480P step: RoPE +
+    append of the current chunk, then attention for `rows_per_head` query
+    rows of every head over the 14040 cached keys.  The cache is built the
+    way the step finds it (chunks at frames 0 and 3 appended first, untimed).
+    Reported in the metric's unit (TFLOP/s of attention)."""
     import numpy as np
     from oracle import attention as A
     from oracle import rope3d as R
     from rope_chunk_causal_amd import synth
 
     nh, D, L, hw = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.hw
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(L, size=rows_per_head, replace=False))
-    q = synth.to_f64(synth.normal((1, rows_per_head, nh, D), 22, "bf16"), "bf16")
-    k = synth.to_f64(synth.normal((1, rows_per_head, nh, D), 23, "bf16"), "bf16")
-    v = synth.to_f64(synth.normal((1, rows_per_head, nh, D), 24, "bf16"), "bf16")
-    kc = synth.to_f64(synth.normal((1, kv, nh, D), 25, "bf16"), "bf16")
-    vc = synth.to_f64(synth.normal((1, kv, nh, D), 26, "bf16"), "bf16")
     r = wl.rope
-    t0 = time.perf_counter()
     tabs = R.rope3d_tables(r.d_t, r.d_h, r.d_w, r.theta, r.max_t, r.max_h, r.max_w)
-    pos = R.positions(wl.frames, wl.height, wl.width, s, 0, L)[rows]
-    qr = R.rope3d_apply(q, tabs, pos)
-    kr = R.rope3d_apply(k, tabs, pos)
-    kc[:, pos[:, 3]] = kr
-    vc[:, pos[:, 3]] = v
-    t_rope = time.perf_counter() - t0
+    kc, vc, _, _ = _oracle_chunks(wl, "480p_step", range(0, s, wl.frames), tabs, kv)
+    q, k, v = (synth.to_f64(synth.normal((1, L, nh, D), synth.seed_for("480p_step", s, 0, x),
+                                         "bf16"), "bf16") for x in ("q", "k", "v"))
     t0 = time.perf_counter()
-    # the sampled queries sit at their own rows of the chunk (q_pos = s*HW)
-    qfull = np.zeros((1, L, nh, D))
-    qfull[:, rows] = qr
-    A.chunk_causal_attention(qfull, kc, vc, s * hw, kv, L, scale, rows=rows)
+    qr = R.rope3d_apply_append(q, k, v, kc, vc, tabs, wl.frames, wl.height, wl.width, s, 0)
+    t_rope = time.perf_counter() - t0
+    rows = np.sort(np.random.default_rng(0).choice(L, size=rows_per_head, replace=False))
+    t0 = time.perf_counter()
+    A.chunk_causal_attention(qr, kc, vc, s * hw, kv, L, scale, rows=rows)
     t_attn = time.perf_counter() - t0
     flops = 4.0 * rows_per_head * kv * D * nh
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count()
+    model, threads = _host_info()
     return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{rows_per_head} of {L} query rows per head x {nh} heads, Lk {kv}, fp64 "
-                      f"numpy: attention {t_attn:.2f} s; RoPE+append of the same tokens "
+                      f"numpy: attention {t_attn:.2f} s; RoPE+append of the whole chunk "
                       f"{t_rope:.2f} s",
             "attn_s": round(t_attn, 3), "rope_s": round(t_rope, 3),
-            "cpu": platform.processor() or platform.machine()}
+            "rope_gbps": round(6.0 * L * nh * D * 2 / t_rope / 1e9, 3), "cpu": model}
+
+
+def cpu_oracle_workloads():
+    """The oracle timed on the host beside the other workloads' GPU figures,
+    each on a stated sample: the SP-rank shard x 64 RoPE + append (whole
+    batch, GB/s of the same algorithmic bytes as the kernel), the 5 s 480P
+    rollout (the last denoising step of each of the 7 chunks, 468 query rows
+    per head, TFLOP/s of attention; the full rollout's time extrapolated from
+    it), and the 720P step (216 query rows per head, TFLOP/s)."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import rope3d as R
+    from rope_chunk_causal_amd import synth
+    model, threads = _host_info()
+    out = {"cpu": model, "cores": threads, "kind": "oracle"}
+
+    sp = synth.WORKLOADS["480p_sp_shard"]
+    n, B, s_sp = sp.chunk_tokens // synth.SP_DEGREE, 64, sp.start_frames[0]
+    r = sp.rope
+    tabs = R.rope3d_tables(r.d_t, r.d_h, r.d_w, r.theta, r.max_t, r.max_h, r.max_w)
+    cap = (s_sp + sp.frames) * sp.hw
+    q, k, v = (synth.to_f64(synth.normal((B, n, sp.n_heads, sp.head_dim), 40 + i, "bf16"), "bf16")
+               for i in range(3))
+    kc = np.zeros((B, cap, sp.n_heads, sp.head_dim))
+    vc = np.zeros_like(kc)
+    t0 = time.perf_counter()
+    R.rope3d_apply_append(q, k, v, kc, vc, tabs, sp.frames, sp.height, sp.width, s_sp, 2 * n)
+    t = time.perf_counter() - t0
+    nbytes = 6.0 * B * n * sp.n_heads * sp.head_dim * 2
+    out["rope_sp_shard_b64"] = {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s",
+                                "s": round(t, 3), "sample": f"whole batch ({B} x {n} tokens)"}
+    del q, k, v, kc, vc
+
+    wl = synth.WORKLOADS["480p_rollout"]
+    nh, D, L, hw = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.hw
+    rows_per_head = 468
+    rows = np.sort(np.random.default_rng(1).choice(L, size=rows_per_head, replace=False))
+    kc = np.zeros((1, wl.cache_tokens(), nh, D))
+    vc = np.zeros_like(kc)
+    t_rope = t_attn = flop = 0.0
+    for s in wl.start_frames:
+        q, k, v = (synth.to_f64(synth.normal((1, L, nh, D),
+                                             synth.seed_for("480p_rollout", s, wl.steps - 1, x),
+                                             "bf16"), "bf16") for x in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        qr = R.rope3d_apply_append(q, k, v, kc, vc, tabs, wl.frames, wl.height, wl.width, s, 0)
+        t_rope += time.perf_counter() - t0
+        kv = (s + wl.frames) * hw
+        t0 = time.perf_counter()
+        A.chunk_causal_attention(qr, kc, vc, s * hw, kv, L, 1.0 / math.sqrt(D), rows=rows)
+        t_attn += time.perf_counter() - t0
+        flop += 4.0 * rows_per_head * kv * D * nh
+    full_flop = sum(4.0 * L * (s + wl.frames) * hw * D * nh for s in wl.start_frames) * wl.steps
+    tf = flop / t_attn / 1e12
+    out["rollout_480p"] = {"value": round(tf, 6), "unit": "TFLOP/s",
+                           "attn_s": round(t_attn, 3), "rope_s": round(t_rope, 3),
+                           "sample": f"last denoising step of each of the {len(wl.start_frames)} "
+                                     f"chunks, {rows_per_head} of {L} query rows per head x "
+                                     f"{nh} heads (RoPE + append of whole chunks)",
+                           "full_rollout_attn_s_extrapolated": round(full_flop / (tf * 1e12), 1)}
+    del kc, vc
+
+    wl = synth.WORKLOADS["720p_step"]
+    D, L, hw = wl.head_dim, wl.chunk_tokens, wl.hw
+    nh = 5          # one GPU's share of the 40 heads split over 8
+    s = wl.start_frames[0]
+    kv = (s + wl.frames) * hw
+    rows_per_head = 1728
+    rows = np.sort(np.random.default_rng(2).choice(L, size=rows_per_head, replace=False))
+    r = wl.rope
+    tabs = R.rope3d_tables(r.d_t, r.d_h, r.d_w, r.theta, r.max_t, r.max_h, r.max_w)
+    kc, vc, qr, _ = _oracle_chunks(wl, "720p_step", list(range(0, s + 1, wl.frames)), tabs, kv,
+                                   n_heads=nh)
+    t0 = time.perf_counter()
+    A.chunk_causal_attention(qr, kc, vc, s * hw, kv, L, 1.0 / math.sqrt(D), rows=rows)
+    t_attn = time.perf_counter() - t0
+    flop = 4.0 * rows_per_head * kv * D * nh
+    out["attn_720p"] = {"value": round(flop / t_attn / 1e12, 6), "unit": "TFLOP/s",
+                        "attn_s": round(t_attn, 3),
+                        "sample": f"{rows_per_head} of {L} query rows per head x {nh} of "
+                                  f"{wl.n_heads} heads, Lk {kv} (cache from the oracle's RoPE + "
+                                  f"append of the 7 chunks, untimed)",
+                        "full_step_s_extrapolated": round(wl.attn_flops(s) / (flop / t_attn), 1)}
+    return out
 
 
 if __name__ == "__main__":

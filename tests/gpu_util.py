@@ -85,3 +85,16 @@ def check_attn(gpu: np.ndarray, ref: np.ndarray, label: str,
 
 def scale_for(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+def wave_rows(n_rows: int, seed: int, tile: int = 256, wave: int = 32) -> np.ndarray:
+    """Query rows that cover every wave of the attention kernels: one seeded
+    random row in each `wave`-row group, plus the first and last row of every
+    `tile`-row query tile (sorted, unique)."""
+    g = np.random.default_rng(seed)
+    starts = np.arange(0, n_rows, wave)
+    ends = np.minimum(starts + wave, n_rows)
+    pick = starts + (g.random(starts.size) * (ends - starts)).astype(np.int64)
+    t0 = np.arange(0, n_rows, tile)
+    edges = np.concatenate([t0, np.minimum(t0 + tile, n_rows) - 1])
+    return np.unique(np.concatenate([pick, edges]))

@@ -1,10 +1,10 @@
 """GPU parity: chunk_causal_attn vs the fp64 oracle.
 
 Element-by-element comparison on seeded inputs: max abs <= 2e-2, mean abs
-<= 2e-3 (bf16 operands, fp32 accumulation) plus a relative L2 bound.  Small
-cases are compared in full; the full-size 480P/720P steps on sampled query
-rows (every head, first/last rows, tile edges).  The oracle sees exactly the
-values the kernel's matrix cores see: for fp32 inputs, their bf16 rounding.
+<= 2e-3 (bf16 operands, fp32 accumulation) plus a relative L2 bound.  These
+cases are compared in full; the full-size 480P and 720P steps are in
+test_gpu_step.py.  The oracle sees exactly the values the kernel's matrix
+cores see: for fp32 inputs, their bf16 rounding.
 """
 import math
 
@@ -80,34 +80,6 @@ def test_ragged_and_masked_shapes(b, lq, nh, d, cap, q_pos, kv, C, in_dt, out_dt
     got, ref, _ = _attn_case(b, lq, nh, d, cap, q_pos, kv, C, in_dt, out_dt, 300 + lq,
                              label="shape")
     check_attn(got, ref, f"{(b, lq, nh, d, q_pos, kv, C)}")
-
-
-def _sample_rows(lq, n, seed):
-    r = np.random.default_rng(seed).choice(lq, size=min(n, lq), replace=False)
-    edges = [0, 1, 31, 32, 127, 128, lq - 129, lq - 128, lq - 2, lq - 1]
-    return np.unique(np.concatenate([r, [e for e in edges if 0 <= e < lq]]))
-
-
-def test_480p_step_full_size_sampled_rows():
-    """Wan-1.3B 480P step: 4680 queries at frames 6..8 over 14040 cached keys."""
-    wl = synth.WORKLOADS["480p_step"]
-    lq = wl.chunk_tokens
-    kv = (6 + 3) * wl.hw
-    rows = _sample_rows(lq, 160, 1)
-    got, ref, _ = _attn_case(1, lq, wl.n_heads, wl.head_dim, kv, 6 * wl.hw, kv, lq,
-                             "bf16", "bf16", 22, rows=rows, label="480p")
-    say("480p", check_attn(got, ref, "480p step"))
-
-
-def test_720p_step_full_size_sampled_rows():
-    """Wan-14B 720P step: 40 heads, 10800 queries over 75600 cached keys."""
-    wl = synth.WORKLOADS["720p_step"]
-    lq = wl.chunk_tokens
-    kv = (18 + 3) * wl.hw
-    rows = _sample_rows(lq, 48, 2)
-    got, ref, _ = _attn_case(1, lq, wl.n_heads, wl.head_dim, kv, 18 * wl.hw, kv, lq,
-                             "bf16", "bf16", 60, rows=rows, label="720p")
-    say("720p", check_attn(got, ref, "720p step"))
 
 
 def test_stress_peaked_softmax():

@@ -201,32 +201,36 @@ def test_sp_shards_bit_equal_unsharded_and_match_oracle():
 
 
 def test_sp_shard_batched_64():
-    """Rank-2 shard with 64 chunks batched (the bandwidth configuration)."""
+    """Rank-2 shard with 64 chunks batched (the bandwidth configuration): every
+    token of every batch entry, and every other cache row keeps its canary."""
     wl = synth.WORKLOADS["480p_sp_shard"]
     s, n, r = 9, 585, 2
     say("sp shard batch 64")
     cfg, host, (qo, kc, vc), cap = _run_apply(wl, s, r * n, n, 64, "bf16", "bf16", 40,
                                               cap=(s + 3) * wl.hw)
-    for b in (0, 17, 63):
-        hb = [x[b:b + 1] for x in host]
-        rq, rk, rv, pos = _oracle_apply(cfg, wl, s, r * n, hb, "bf16", cap)
-        check_bf16_rope(to_host_f64(qo[b:b + 1]), rq, f"b{b} q'")
-        check_bf16_rope(to_host_f64(kc[b:b + 1])[:, pos[:, 3]], rk, f"b{b} k")
-        assert np.array_equal(to_host_f64(vc[b:b + 1])[:, pos[:, 3]], rv)
+    rq, rk, rv, pos = _oracle_apply(cfg, wl, s, r * n, host, "bf16", cap)
+    check_bf16_rope(to_host_f64(qo), rq, "b64 q'")
+    gk, gv = to_host_f64(kc), to_host_f64(vc)
+    check_bf16_rope(gk[:, pos[:, 3]], rk, "b64 k")
+    assert np.array_equal(gv[:, pos[:, 3]], rv)
+    other = np.setdiff1d(np.arange(cap), pos[:, 3])
+    assert np.all(gk[:, other] == 3.0) and np.all(gv[:, other] == -3.0)
 
 
-def test_apply_720p_sampled_tokens():
-    """Wan-14B 720P chunk (40 heads, 10800 tokens) at frames 18..20: sampled tokens."""
+def test_apply_720p_every_token():
+    """Wan-14B 720P chunk (40 heads, 10800 tokens) at frames 18..20: every token,
+    and every cache row outside the chunk keeps its canary."""
     wl = synth.WORKLOADS["720p_step"]
     s = 18
     say("apply 720p")
     cfg, host, (qo, kc, vc), cap = _run_apply(wl, s, 0, wl.chunk_tokens, 1, "bf16", "bf16", 60)
-    tok = np.sort(np.random.default_rng(5).choice(wl.chunk_tokens, 700, replace=False))
-    tok = np.unique(np.concatenate([tok, [0, 1, 3599, 3600, wl.chunk_tokens - 1]]))
-    rq, rk, rv, pos = _oracle_apply(cfg, wl, s, 0, host, "bf16", cap, tokens=tok)
-    check_bf16_rope(to_host_f64(qo[:, tok]), rq, "720p q'")
-    check_bf16_rope(to_host_f64(kc[:, pos[:, 3]]), rk, "720p k")
-    assert np.array_equal(to_host_f64(vc[:, pos[:, 3]]), rv)
+    rq, rk, rv, pos = _oracle_apply(cfg, wl, s, 0, host, "bf16", cap)
+    check_bf16_rope(to_host_f64(qo), rq, "720p q'")
+    gk, gv = to_host_f64(kc), to_host_f64(vc)
+    check_bf16_rope(gk[:, pos[:, 3]], rk, "720p k")
+    assert np.array_equal(gv[:, pos[:, 3]], rv)
+    other = np.setdiff1d(np.arange(cap), pos[:, 3])
+    assert np.all(gk[:, other] == 3.0) and np.all(gv[:, other] == -3.0)
 
 
 def test_in_place_q_and_determinism():
