@@ -164,6 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
   // No load may still be writing this workgroup's LDS when it exits.
   __builtin_amdgcn_s_waitcnt(0);
 
+  finish_rows<true>(w);
   if (qrow < a.q_tokens) store_row(w, og + (int64_t)qrow * rs, g);
 }
 

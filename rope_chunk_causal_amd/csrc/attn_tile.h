@@ -26,7 +26,12 @@ constexpr int kBN = 32;                      // keys per tile
 constexpr int kRowBytes = kD * 2;            // 256 B per key row
 constexpr int kTileBytes = kBN * kRowBytes;  // 8 KB
 constexpr int kXcds = 8;
-constexpr float kLazy = 8.0f;                // log2 headroom before a rescale
+constexpr float kLazy = 8.0f;                // log2 headroom before a rescale (classic)
+// Base-2 scheme: the reference moves when a tile's max exceeds it by more
+// than 2^48; a lane's 16 probabilities of a tile are checked through their
+// sum, which stays below 2^56 unless one of them passed 2^52.
+constexpr float kMoveT = 48.0f;
+constexpr float kSumCap = 72057594037927936.0f;  // 2^56
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -70,11 +75,21 @@ __device__ __forceinline__ void tile_ready() {
 //
 // Two bookkeeping schemes for the scores, chosen per kernel (kBase2):
 // * classic: S^T = K Q^T from the bf16 q; a score's probability is
-//   exp2(s * c2 - m_run) with c2 = scale * log2(e) (one fma per score);
+//   exp2(s * c2 - m_run) with c2 = scale * log2(e) (one fma per score); the
+//   reference max moves when a tile's max exceeds it by more than 2^8, and
+//   l_run is the row's sum.
 // * base-2 accumulation: q is pre-multiplied by c2 (load_q<true>) and the
 //   S^T accumulation starts from negm = -m_run, so the MFMA results are
 //   already s * c2 - m_run and a score's probability is exp2 of it, with
-//   no VALU op before the exponential.  It needs 16 more VGPRs (negm).
+//   no VALU op before the exponential.  It needs 16 more VGPRs (negm).  No
+//   tile max is taken in the common case: the reference is set from the
+//   first tile that gives the row weight, and afterwards moves only when a
+//   lane's probability sum of a tile leaves [0, 2^56] (a score more than
+//   2^52 above the reference, or a NaN/inf) and the tile max is then more
+//   than 2^48 above it.  Probabilities thus stay below 2^56 (finite in bf16
+//   and in the fp32 sums), and the reference never exceeds the row max, so
+//   the row's largest probability is at least 1.  l_run is the lane's half
+//   of the row sum (its 16 keys of each tile); finish_rows adds the halves.
 struct WaveState {
   f32x16 oacc[4];
   f32x16 negm;          // -m_run in every element (base-2 scheme only)
@@ -176,33 +191,54 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) vf[kq][dt] = vread(kq, dt);
 
-  float mx = s0[0];
-#pragma unroll
-  for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);  // v_max3_f32
-  mx = fmaxf(mx, s0[15]);
-  mx = xhalf_max(mx);
+  bf16x8 pf[2];
   if constexpr (kBase2) {
-    // mx is the tile max relative to the reference.  Lazy rescale: move the
-    // reference only when the max would exceed it by more than 2^8, or,
-    // before the row has any weight, to the first finite max (so that very
-    // negative scores do not all underflow).
-    const bool move = mx > kLazy || (w.l_run == 0.f && mx > -INFINITY);
-    if (__ballot(move)) {
+    float p[16];
+    float rsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(s0[r]);
+      rsum += p[r];
+    }
+    // Rare path: a probability may pass 2^52 (or is not finite), or the row
+    // has no weight yet; then take the tile max and move the reference if
+    // it is more than 2^48 above it, or if the row has no weight (to the
+    // first finite max, so that uniformly very negative scores do not all
+    // underflow).  Lanes l and l + 32 hold the same row and decide alike.
+    if (__ballot(!(rsum <= kSumCap) || w.l_run == 0.f)) {
+      float mx = s0[0];
+#pragma unroll
+      for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);
+      mx = fmaxf(mx, s0[15]);
+      mx = xhalf_max(mx);
+      const float l_row = xhalf_sum(w.l_run);
+      const bool move = mx > kMoveT || (l_row == 0.f && mx > -INFINITY);
       const float shift = move ? mx : 0.f;
-      const float alpha = w.l_run == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
+      const float alpha = l_row == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
       w.l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
+      rsum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s0[r] -= shift;
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(s0[r] - shift);
+        rsum += p[r];
+      }
       w.m_run += shift;
 #pragma unroll
       for (int r = 0; r < 16; ++r) w.negm[r] = -w.m_run;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)p[r];
+    w.l_run += rsum;
   } else {
-    mx *= c2;
+    float mx = s0[0];
+#pragma unroll
+    for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);  // v_max3_f32
+    mx = fmaxf(mx, s0[15]);
+    mx = xhalf_max(mx) * c2;
     // Lazy rescale: move the reference max only when it would grow by > 2^8.
     const float m_use = (mx - w.m_run > kLazy) ? mx : w.m_run;
     if (__ballot(m_use != w.m_run)) {
@@ -214,23 +250,27 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
         for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
       w.m_run = m_use;
     }
-  }
-
-  float rsum = 0.f;
-  bf16x8 pf[2];
+    float rsum = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = kBase2 ? __builtin_amdgcn_exp2f(s0[r])
-                           : __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -w.m_run));
-    rsum += p;
-    pf[r >> 3][r & 7] = (__bf16)p;
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -w.m_run));
+      rsum += p;
+      pf[r >> 3][r & 7] = (__bf16)p;
+    }
+    w.l_run += xhalf_sum(rsum);
   }
-  w.l_run += xhalf_sum(rsum);
 
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) w.oacc[dt] = mfma32(vf[kq][dt], pf[kq], w.oacc[dt]);
+}
+
+// Base-2 scheme: l_run becomes the row's sum (both lanes of the row take
+// part; call it with every lane of the wave active).
+template <bool kBase2>
+__device__ __forceinline__ void finish_rows(WaveState& w) {
+  if constexpr (kBase2) w.l_run = xhalf_sum(w.l_run);
 }
 
 // O / l for the lane's query row (column of O^T), stored to orow.  A row that
