@@ -227,6 +227,8 @@ def main():
     rolling = rolling_rollout(rcc, synth, cfg, tables, randn, stream, dev)
     sparse = block_sparse(rcc, synth, randn, stream, dev)
     attn720 = attn_720p(rcc, synth, randn, stream, dev)
+    attn720_long = attn_720p_long_cache(rcc, synth, randn, stream, dev)
+    occupancy = attn_occupancy(rcc, synth, randn, stream, dev)
 
     traffic = read_traffic("chunk_causal_attn_480p_step")
     result = {
@@ -263,6 +265,8 @@ def main():
         "rolling_1min": rolling,
         "block_sparse": sparse,
         "attn_720p": attn720,
+        "attn_720p_cache_past_4gib": attn720_long,
+        "attn_occupancy": occupancy,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -524,6 +528,67 @@ def attn_720p(rcc, synth, randn, stream, dev):
     torch.cuda.empty_cache()
     return {"ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "q_tokens": L,
             "kv_tokens": kv, "heads": nh, "frac_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def attn_720p_long_cache(rcc, synth, randn, stream, dev):
+    """chunk_causal_attn at 720P late in a long video: the chunk at frames
+    117..119 over a cache that keeps all 120 frames (432000 keys x 40 heads,
+    4.4 GB each for K and V, past 4 GiB per batch entry), on the same
+    bf16 head_dim-128 kernel as every other step; 1 untimed launch, then 3
+    timed with HIP events on the launch stream."""
+    import torch
+    wl = synth.WORKLOADS["720p_step"]
+    nh, D, L, hw = wl.n_heads, wl.head_dim, wl.chunk_tokens, wl.hw
+    s = 117
+    kv = (s + wl.frames) * hw
+    q = randn(1, L, nh, D)
+    k = torch.empty(1, kv, nh, D, device=dev, dtype=torch.bfloat16)
+    v = torch.empty_like(k)
+    for t in (k, v):       # fill frame by frame (bounded temporaries)
+        for f0 in range(0, kv, 12 * hw):
+            n = min(12 * hw, kv - f0)
+            t[:, f0:f0 + n] = randn(1, n, nh, D)
+    o = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(D)
+
+    def run(i):
+        rcc.chunk_causal_attn(q, k, v, o, s * hw, kv, L, scale, stream=stream)
+    run(0)
+    ms = _time_events(run, stream, 3)
+    flop = 4.0 * L * kv * D * nh
+    entry_bytes = kv * nh * D * 2
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "q_tokens": L,
+            "kv_tokens": kv, "heads": nh, "k_cache_bytes_per_entry": entry_bytes,
+            "past_4gib": entry_bytes > (1 << 32),
+            "frac_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def attn_occupancy(rcc, synth, randn, stream, dev):
+    """The 480P attention shape with 1, 4, 8, 10 and 12 heads (19 query tiles
+    per head, one round of workgroups): the same work per workgroup at every
+    size.  A launch that takes longer with more busy CUs is held by the
+    chip's power limit, not by the grid.  10 timed launches each."""
+    wl = synth.WORKLOADS["480p_step"]
+    s = wl.start_frames[0]
+    L, D, hw = wl.chunk_tokens, wl.head_dim, wl.hw
+    kv = (s + wl.frames) * hw
+    out = {}
+    for nh in (1, 4, 8, 10, 12):
+        q = randn(1, L, nh, D)
+        k = randn(1, kv, nh, D)
+        v = randn(1, kv, nh, D)
+        o = q.clone()
+
+        def run(i):
+            rcc.chunk_causal_attn(q, k, v, o, s * hw, kv, L, 1.0 / math.sqrt(D), stream=stream)
+        for i in range(3):
+            run(i)
+        ms = _time_events(run, stream, 10)
+        out[f"heads_{nh}"] = {"busy_cus": 19 * nh, "ms": round(ms, 4),
+                              "tflops": round(4.0 * L * kv * D * nh / (ms * 1e-3) / 1e12, 1)}
+    return out
 
 
 def block_sparse(rcc, synth, randn, stream, dev):
