@@ -110,6 +110,52 @@ def test_stress_dominant_key_late():
     check_attn(to_host_f64(out), ref, "dominant key")
 
 
+def _directed_case(seed, q_shift, key_shift):
+    """q rows N(0,1) + q_shift * u and keys N(0,1) + key_shift[j] * u for a
+    seeded unit vector u: logits (q.k)/sqrt(d) follow key_shift along the keys."""
+    lq, kv, d = 128, 2048, 128
+    g = np.random.Generator(np.random.PCG64(seed))
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = synth.bf16_bits_to_f32(synth.normal((1, lq, 1, d), seed + 1, "bf16")) + q_shift * u
+    k = synth.bf16_bits_to_f32(synth.normal((1, kv, 1, d), seed + 2, "bf16"))
+    k += np.asarray(key_shift, dtype=np.float32)[None, :, None, None] * u
+    v = synth.normal((1, kv, 1, d), seed + 3, "bf16")
+    qb = synth.f32_to_bf16_bits(q.astype(np.float32))
+    kb = synth.f32_to_bf16_bits(k.astype(np.float32))
+    t = torch()
+    out = t.full((1, lq, 1, d), float("nan"), dtype=t.float32, device="cuda")
+    say("directed scores", seed, q_shift)
+    rcc.chunk_causal_attn(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(v, "bf16"), out,
+                          kv - lq, kv, kv, 1 / math.sqrt(d))
+    t.cuda.synchronize()
+    ref = A.chunk_causal_attention(synth.to_f64(qb, "bf16"), synth.to_f64(kb, "bf16"),
+                                   synth.to_f64(v, "bf16"), kv - lq, kv, kv, 1 / math.sqrt(d))
+    return to_host_f64(out), ref
+
+
+def test_stress_scores_rise_then_jump_past_fp32_range():
+    """Logits that climb tile by tile (the softmax reference must move several
+    times), then two keys whose base-2 scores sit ~300 above the reference, so
+    their exponentials overflow fp32 before the reference catches up, then
+    ordinary keys again.  The output mixes the two top keys' values."""
+    shift = np.zeros(2048)
+    shift[1000:1400] = np.arange(400) * 0.2          # a ramp over 12 key tiles
+    shift[1500], shift[1700] = 400.0, 400.5          # far above everything else
+    got, ref = _directed_case(910, 6.0, shift)
+    assert np.isfinite(got).all()
+    say("rise/jump", check_attn(got, ref, "rise then jump"))
+
+
+def test_stress_all_scores_far_below_zero():
+    """Every logit near -210 (base-2 scores near -300): each probability
+    underflows to zero against the initial reference, so the reference must
+    be taken from the first tile's max."""
+    got, ref = _directed_case(920, -6.0, np.full(2048, 400.0))
+    assert np.isfinite(got).all()
+    say("all negative", check_attn(got, ref, "all far below zero"))
+
+
 def test_determinism_and_no_nan():
     t = torch()
     q = to_dev(synth.normal((1, 700, 4, 128), 700, "bf16"), "bf16")
