@@ -27,9 +27,10 @@ constexpr int kRowBytes = kD * 2;            // 256 B per key row
 constexpr int kTileBytes = kBN * kRowBytes;  // 8 KB
 constexpr int kXcds = 8;
 constexpr float kLazy = 8.0f;                // log2 headroom before a rescale (classic)
-// Base-2 scheme: the reference moves when a tile's max exceeds it by more
-// than 2^48; a lane's 16 probabilities of a tile are checked through their
-// sum, which stays below 2^56 unless one of them passed 2^52.
+// Base-2 scheme (scores are base-2 exponents): the reference moves when a
+// tile's max exceeds it by more than 48, i.e. a probability passes 2^48; a
+// lane's 16 probabilities of a tile are checked through their sum, which
+// stays below 2^56 unless one of them passed 2^52.
 constexpr float kMoveT = 48.0f;
 constexpr float kSumCap = 72057594037927936.0f;  // 2^56
 
@@ -84,9 +85,9 @@ __device__ __forceinline__ void tile_ready() {
 //   no VALU op before the exponential.  It needs 16 more VGPRs (negm).  No
 //   tile max is taken in the common case: the reference is set from the
 //   first tile that gives the row weight, and afterwards moves only when a
-//   lane's probability sum of a tile leaves [0, 2^56] (a score more than
-//   2^52 above the reference, or a NaN/inf) and the tile max is then more
-//   than 2^48 above it.  Probabilities thus stay below 2^56 (finite in bf16
+//   lane's probability sum of a tile leaves [0, 2^56] (a probability above
+//   2^52, i.e. a score more than 52 above the reference, or a NaN/inf) and
+//   the tile max is then more than 48 above it.  Probabilities thus stay below 2^56 (finite in bf16
 //   and in the fp32 sums), and the reference never exceeds the row max, so
 //   the row's largest probability is at least 1.  l_run is the lane's half
 //   of the row sum (its 16 keys of each tile); finish_rows adds the halves.
@@ -202,7 +203,7 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
     }
     // Rare path: a probability may pass 2^52 (or is not finite), or the row
     // has no weight yet; then take the tile max and move the reference if
-    // it is more than 2^48 above it, or if the row has no weight (to the
+    // it is more than 48 above it, or if the row has no weight (to the
     // first finite max, so that uniformly very negative scores do not all
     // underflow).  Lanes l and l + 32 hold the same row and decide alike.
     if (__ballot(!(rsum <= kSumCap) || w.l_run == 0.f)) {
