@@ -48,20 +48,29 @@ def parse():
     return p.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed: what the
+    compiler sees, so that editing a comment keeps the hash."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of what the attention kernels are compiled from: their sources,
-    and from the shared internal header the vector typedefs and the
-    attention argument struct (the rest of that header serves other
-    kernels)."""
+    """Hash of what the attention kernels are compiled from (comments and
+    whitespace ignored): their sources, and from the shared internal header
+    the vector typedefs and the attention argument struct (the rest of that
+    header serves other kernels)."""
     import re
     csrc = os.path.join(ROOT, "rope_chunk_causal_amd", "csrc")
     h = hashlib.sha256()
     for f in ("attn.hip", "attn_d128.hip", "attn_tile.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     text = open(os.path.join(csrc, "rcc_internal.h")).read()
     for m in re.finditer(r"^typedef [^\n]*;$|^struct AttnArgs \{.*?^\};", text, re.M | re.S):
-        h.update(m.group(0).encode())
+        h.update(_code_only(m.group(0)).encode())
     return h.hexdigest()[:16]
 
 

@@ -87,9 +87,9 @@ __device__ __forceinline__ void tile_ready() {
 //   first tile that gives the row weight, and afterwards moves only when a
 //   lane's probability sum of a tile leaves [0, 2^56] (a probability above
 //   2^52, i.e. a score more than 52 above the reference, or a NaN/inf) and
-//   the tile max is then more than 48 above it.  Probabilities thus stay below 2^56 (finite in bf16
-//   and in the fp32 sums), and the reference never exceeds the row max, so
-//   the row's largest probability is at least 1.  l_run is the lane's half
+//   the tile max is then more than 48 above it.  Probabilities thus stay
+//   below 2^56 (finite in bf16 and in the fp32 sums), and the reference never
+//   exceeds the row max, so the row's largest probability is at least 1.  l_run is the lane's half
 //   of the row sum (its 16 keys of each tile); finish_rows adds the halves.
 struct WaveState {
   f32x16 oacc[4];
