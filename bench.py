@@ -603,9 +603,11 @@ def attn_occupancy(rcc, synth, randn, stream, dev):
 def block_sparse(rcc, synth, randn, stream, dev):
     """Block-sparse attention on the Sparse Forcing-shaped memory (query
     chunk of 84 blocks of 64 tokens, 168 persistent + 336 local-window blocks,
-    12 heads) at Top-K 25 / 12.5 / 6.25 % of the window, beside the dense
-    kernel over the whole memory (every key visible).  TFLOP/s counts the
-    selected query-key pairs only.  HIP events on the launch stream."""
+    12 heads; and the same token counts in [3,4,4] blocks of 48: 112 query,
+    224 persistent and 448 window blocks) at Top-K 25 / 12.5 / 6.25 % of the
+    window, beside the dense kernel over the whole memory (every key
+    visible).  TFLOP/s counts the selected query-key pairs only.  HIP events
+    on the launch stream."""
     import numpy as np
     import torch
     out = {}
@@ -623,7 +625,7 @@ def block_sparse(rcc, synth, randn, stream, dev):
         dense(i)
     d_ms = _time_events(dense, stream, 20)
     d_flop = 4.0 * w0.q_tokens * w0.kv_tokens * w0.head_dim * w0.n_heads
-    for name, w in synth.SPARSE_WORKLOADS.items():
+    for name, w in list(synth.SPARSE_WORKLOADS.items()) + list(synth.SPARSE_WORKLOADS_344.items()):
         p, l = synth.block_lists(w, 7)
         dp = torch.from_numpy(p).to(dev)
         dl = torch.from_numpy(np.ascontiguousarray(l)).to(dev)

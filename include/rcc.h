@@ -359,7 +359,9 @@ RCC_API rcc_status rcc_chunk_causal_attn_ring(
  *   local    int32 [batch, n_heads, ceil(q_tokens / B), n_local] device:
  *            the key blocks each query block adds.
  *   out      [batch, q_tokens, n_heads, 128] in `out_dtype`.
- * B = block_tokens.  Query block i attends the union of its two lists:
+ * B = block_tokens: 32, 48, 64, 128 or 256 (48 is [SF]'s [3,4,4] block and
+ * 64 its [1,8,8]; a block is B consecutive rows whatever its shape).  Query
+ * block i attends the union of its two lists:
  * repeated entries count once and entries outside [0, kv_tokens / B)
  * are ignored (-1 pads a list).  out = softmax(scale * q k^T) v over the
  * union's keys, fp32 softmax and accumulation, bf16 matrix-core operands;
@@ -369,7 +371,7 @@ RCC_API rcc_status rcc_chunk_causal_attn_ring(
  * padding, so neither changes a bit of the result.
  * Errors: NULL (a tensor, or a list whose length is non-zero); DTYPE
  * (in_dtype not bf16, unknown out_dtype); SHAPE (head_dim != 128,
- * block_tokens not 32, 64, 128 or 256, batch/n_heads non-positive,
+ * block_tokens not 32, 48, 64, 128 or 256, batch/n_heads non-positive,
  * q_tokens/kv_tokens/n_persist/n_local negative, n_persist + n_local >
  * 1024, kv_tokens / B > 32768, scale not positive and finite); RANGE
  * (kv_tokens > cache_tokens);

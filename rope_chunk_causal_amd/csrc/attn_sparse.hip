@@ -11,7 +11,8 @@
 //
 // Design for gfx950:
 // * Blocks of 64, 128 or 256 rows (attn_sparse_grouped_kernel): one 8-wave
-//   workgroup per G = 8 / (B / 32) query blocks of one (batch, head).  The
+//   workgroup per G = 8 / (B / 32) query blocks of one (batch, head); blocks
+//   of 48 rows: one 4-wave workgroup per two query blocks.  The
 //   persistent blocks, common to every query block, stream once for the
 //   whole workgroup: all 8 waves share each K/V tile (four LDS stages, three
 //   tiles in flight), so a tile moves into LDS once per 256 query rows, as in
@@ -25,15 +26,18 @@
 //   compacted in ascending order with a wave-level scan.  The visit order
 //   thus depends only on the sets, never on how the lists are ordered or
 //   padded.
-// * B is a multiple of the 32-key tile, so every tile lies inside one key
-//   block: tile t of a list reads rows list[t / (B/32)] * B + 32 (t % (B/32))
-//   + [0, 32).  No partial tiles and no masking; the per-tile MFMA and
-//   softmax work is attn_tile.h's, shared with the dense kernel.
+// * A list's blocks are read as one key stream of 32-row tiles.  For B a
+//   multiple of 32 every tile lies inside one block: no partial tiles and no
+//   masking.  For B = 48 a tile may span two blocks (three tiles per two
+//   blocks) and only a list's last tile can be partial (its keys past the
+//   stream are masked).  The per-tile MFMA and softmax work is attn_tile.h's,
+//   shared with the dense kernel.
 // * K/V tiles stream global -> LDS with global_load_lds_dwordx4, branch-free
 //   (the tile index is clamped to the last tile, so the wait counts stay
-//   exact), into one __shared__ object per stage.  A tile's first row gives a
-//   wave-uniform 64-bit base and lanes add 32-bit offsets inside the tile, so
-//   a batch entry's cache may exceed 4 GiB.
+//   exact), into one __shared__ object per stage.  Row offsets are formed in
+//   64 bits (a wave-uniform base plus 32-bit lane offsets inside a block, or
+//   per lane where a tile spans two blocks), so a batch entry's cache may
+//   exceed 4 GiB.
 // * Workgroups are numbered XCD-major: the query blocks of one head run on
 //   one XCD and share its L2.
 #include <type_traits>
@@ -203,11 +207,13 @@ __global__ __launch_bounds__(64 * NW, NW > 1 ? 2 : 1) void attn_sparse_kernel(Sp
   if (qrow < a.q_tokens) store_row(w, og + (int64_t)qrow * rs, g);
 }
 
-// Compact a bitmap over key blocks into an ascending list (all 512 threads
-// of the workgroup take part); returns the number of set bits.
-__device__ __forceinline__ int compact512(const uint32_t* bm, int words, int* out, int tid,
-                                          int lane, int wave, int* s_tot) {
-  const int wpt = (words + 511) / 512;
+// Compact a bitmap over key blocks into an ascending list (all 64 * NW
+// threads of the workgroup take part); returns the number of set bits.
+template <int NW>
+__device__ __forceinline__ int compact_list(const uint32_t* bm, int words, int* out, int tid,
+                                            int lane, int wave, int* s_tot) {
+  constexpr int kT = 64 * NW;
+  const int wpt = (words + kT - 1) / kT;
   const int w0 = tid * wpt;
   int cnt = 0;
   for (int i = 0; i < wpt; ++i)
@@ -222,7 +228,7 @@ __device__ __forceinline__ int compact512(const uint32_t* bm, int words, int* ou
   __syncthreads();
   int pos = incl - cnt, total = 0;
 #pragma unroll
-  for (int w2 = 0; w2 < 8; ++w2) {
+  for (int w2 = 0; w2 < NW; ++w2) {
     const int tot = s_tot[w2];
     pos += w2 < wave ? tot : 0;
     total += tot;
@@ -239,31 +245,103 @@ __device__ __forceinline__ int compact512(const uint32_t* bm, int words, int* ou
   return __builtin_amdgcn_readfirstlane(total);
 }
 
-// Grouped variant for blocks of 64, 128 or 256 rows: one 8-wave workgroup
-// takes G = 8 / NWB query blocks of one (batch, head) (NWB = B / 32 waves per
-// block).  The persistent blocks, common to all of them, stream once for the
-// whole workgroup (all 8 waves share each tile; four LDS stages, three tiles
-// in flight, as in the dense kernel).  Then every query block streams its own
-// local blocks, minus those already in the persistent set, through SL stages
-// of its own; the blocks advance in lockstep (one workgroup barrier per tile),
-// and a block with fewer tiles idles at the barriers.
-template <typename Tout, int NWB>
-__global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs a, int n_groups) {
-  constexpr int G = 8 / NWB;
-  constexpr int SL = G == 4 ? 2 : 4;
-  constexpr int B = 32 * NWB;
-  constexpr int kLWait = (SL - 2) * 2 * (8 / NWB);
+// Issue DMA instructions i = i0, i0 + di, ... (NI of them) of tile t of a
+// list of n >= 1 key blocks.  The list's blocks are read as one key stream,
+// laid end to end: tile t is stream rows 32 t .. 32 t + 31, and rows past the
+// stream's end repeat its last row (their scores are masked).  t is clamped
+// to the last tile (the pipeline runs ahead).  Instruction i moves tile rows
+// 4 i .. 4 i + 3 into LDS bytes [i KB, +1 KB); lane -> (row 4 i + lane/16,
+// chunk slot lane%16).  For B a multiple of 32 a tile lies inside one block
+// and a wave-uniform 64-bit base plus 32-bit lane offsets address it; for
+// B = 48 a tile spans at most two blocks and each lane forms its row's 64-bit
+// offset itself.
+template <int B, int NI>
+__device__ __forceinline__ void issue_list(const char* kg, const char* vg, uint32_t row_bytes,
+                                           const int* list, int n, int t, char* ks, int i0,
+                                           int di, int lane) {
+  const int n_tiles = (n * B + 31) / 32;
+  t = __builtin_amdgcn_readfirstlane(min(t, n_tiles - 1));
+  if constexpr (B % 32 == 0) {
+    constexpr int kPer = B / 32;
+    const int blk = __builtin_amdgcn_readfirstlane(list[t / kPer]);
+    const int64_t base = (int64_t)(blk * B + (t % kPer) * 32) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int i = i0 + di * j;
+      const int r = 4 * i + (lane >> 4);
+      const uint32_t off = (uint32_t)r * row_bytes;
+      __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
+                                       (lds_void*)(ks + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
+                                       (lds_void*)(ks + kTileBytes + i * 1024), 16, 0, 0);
+    }
+  } else {
+    static_assert(B > 32 && B < 64, "a tile spans at most two blocks");
+    const int g0 = 32 * t;
+    const int last = n * B - 1;
+    const int b_lo = g0 / B;
+    const int b_hi = min(g0 + 31, last) / B;
+    const int blk_lo = __builtin_amdgcn_readfirstlane(list[b_lo]);
+    const int blk_hi = __builtin_amdgcn_readfirstlane(list[b_hi]);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int i = i0 + di * j;
+      const int r = 4 * i + (lane >> 4);
+      const int gr = min(g0 + r, last);
+      const int bi = gr / B;
+      const int row = (bi == b_lo ? blk_lo : blk_hi) * B + (gr - bi * B);
+      const int64_t off = (int64_t)row * row_bytes;
+      __builtin_amdgcn_global_load_lds(kg + off + k_chunk(r, lane & 15),
+                                       (lds_void*)(ks + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + off + v_chunk(r, lane & 15),
+                                       (lds_void*)(ks + kTileBytes + i * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// Grouped variant for blocks of 48, 64, 128 or 256 rows: one NW-wave
+// workgroup takes G = NW / NWB query blocks of one (batch, head), NWB =
+// ceil(B / 32) waves per block.  The persistent blocks, common to all of
+// them, stream once for the whole workgroup (every wave shares each tile;
+// four LDS stages, three tiles in flight, as in the dense kernel).  Then
+// every query block streams its own local blocks, minus those already in the
+// persistent set, through SL stages of its own; the blocks advance in
+// lockstep (one workgroup barrier per tile), and a block with fewer tiles
+// idles at the barriers.
+//
+// Blocks of 48 rows ([SF]'s [3,4,4]) run 4-wave workgroups of two query
+// blocks (64 KB of stages, two workgroups per CU; 112 blocks per head make
+// 1344 of them at 12 heads, so finer work evens out the last round), and
+// read each list as a key stream of 32-row tiles across block boundaries:
+// three tiles per two blocks, only a list's last tile partial and masked.  A
+// block's second wave holds its rows 32 .. 47; its other 16 rows are
+// computed but not stored.
+template <typename Tout, int NW, int NWB, int B>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attn_sparse_grouped_kernel(
+    SparseArgs a, int n_groups) {
+  static_assert(NW == 8 || NW == 4, "4 or 8 waves");
+  static_assert(B == 32 * NWB || (B == 48 && NWB == 2), "block of 48, 64, 128 or 256 rows");
+  constexpr int kT = 64 * NW;
+  constexpr int G = NW / NWB;
+  constexpr int kObjs = NW == 8 ? 8 : 4;              // 16 KB stage objects
+  constexpr int SL = kObjs / G < 4 ? kObjs / G : 4;   // local stages per query block
+  constexpr bool kGather = B % 32 != 0;
+  constexpr int kPI = 8 / NW;                         // DMA instructions per wave per tensor
+  constexpr int kLI = 8 / NWB;                        //   (persistent, local phase)
+  constexpr int kPWait = 2 * 2 * kPI;                 // loads of tiles t+1, t+2
+  constexpr int kLWait = (SL - 2) * 2 * kLI;          // loads of tiles t+1 .. t+SL-2
+  static_assert(SL >= 2 && 1 + G <= kObjs, "stages for the lists' bitmaps and the local phase");
   __shared__ __align__(1024) char sS0[2 * kTileBytes];
   __shared__ __align__(1024) char sS1[2 * kTileBytes];
   __shared__ __align__(1024) char sS2[2 * kTileBytes];
   __shared__ __align__(1024) char sS3[2 * kTileBytes];
-  __shared__ __align__(1024) char sS4[2 * kTileBytes];
-  __shared__ __align__(1024) char sS5[2 * kTileBytes];
-  __shared__ __align__(1024) char sS6[2 * kTileBytes];
-  __shared__ __align__(1024) char sS7[2 * kTileBytes];
+  __shared__ __align__(1024) char sS4[kObjs > 4 ? 2 * kTileBytes : 16];
+  __shared__ __align__(1024) char sS5[kObjs > 5 ? 2 * kTileBytes : 16];
+  __shared__ __align__(1024) char sS6[kObjs > 6 ? 2 * kTileBytes : 16];
+  __shared__ __align__(1024) char sS7[kObjs > 7 ? 2 * kTileBytes : 16];
   __shared__ int s_plist[kMaxSel];
   __shared__ int s_llist[G][kMaxSel];
-  __shared__ int s_tot[8];
+  __shared__ int s_tot[NW];
   auto stage = [&](int u) -> char* {
     return u == 0 ? sS0 : u == 1 ? sS1 : u == 2 ? sS2 : u == 3 ? sS3
          : u == 4 ? sS4 : u == 5 ? sS5 : u == 6 ? sS6 : sS7;
@@ -292,7 +370,8 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
       reinterpret_cast<const __bf16*>(a.v) + (int64_t)b * a.cache_tokens * rs + h * kD);
   Tout* og = reinterpret_cast<Tout*>(a.out) + (int64_t)b * a.q_tokens * rs + h * kD;
 
-  const int qrow = (qb0 + jw) * B + wq * 32 + l32;
+  const int brow = wq * 32 + l32;       // the lane's row inside its query block
+  const int qrow = (qb0 + jw) * B + brow;
   const int qclamp = qrow < a.q_tokens ? qrow : a.q_tokens - 1;
   bf16x8 qf[8];
   load_q<false>(qf, qg, rs, qclamp, g, a.scale_log2);
@@ -302,19 +381,19 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
   const int words = (a.n_kblocks + 31) >> 5;
   uint32_t* pbm = reinterpret_cast<uint32_t*>(sS0);
   auto lbm = [&](int jj) { return reinterpret_cast<uint32_t*>(stage(1 + jj)); };
-  for (int i = tid; i < words; i += 512) {
+  for (int i = tid; i < words; i += kT) {
     pbm[i] = 0u;
 #pragma unroll
     for (int jj = 0; jj < G; ++jj) lbm(jj)[i] = 0u;
   }
   __syncthreads();
   const int* pl = a.persist + (int64_t)bh * a.n_persist;
-  for (int e = tid; e < a.n_persist; e += 512) {
+  for (int e = tid; e < a.n_persist; e += kT) {
     const int x = pl[e];
     if ((unsigned)x < (unsigned)a.n_kblocks) atomicOr(&pbm[x >> 5], 1u << (x & 31));
   }
   __syncthreads();
-  for (int e = tid; e < G * a.n_local; e += 512) {
+  for (int e = tid; e < G * a.n_local; e += kT) {
     const int jj = e / a.n_local;
     const int qbj = qb0 + jj;
     if (qbj >= a.n_qblocks) continue;
@@ -323,10 +402,11 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
       atomicOr(&lbm(jj)[x >> 5], 1u << (x & 31));
   }
   __syncthreads();
-  const int n_p = compact512(pbm, words, s_plist, tid, lane, wave, s_tot);
+  const int n_p = compact_list<NW>(pbm, words, s_plist, tid, lane, wave, s_tot);
   int n_l[G];
 #pragma unroll
-  for (int jj = 0; jj < G; ++jj) n_l[jj] = compact512(lbm(jj), words, s_llist[jj], tid, lane, wave, s_tot);
+  for (int jj = 0; jj < G; ++jj)
+    n_l[jj] = compact_list<NW>(lbm(jj), words, s_llist[jj], tid, lane, wave, s_tot);
 
   Lane L;
   lane_setup(L, lane);
@@ -334,30 +414,30 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
   wave_init<false>(w);
   const float c2 = a.scale_log2;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
+  // Tile t of a key stream of n_rows rows (only a 48-row block's stream has a
+  // partial last tile: keys at or past L.lim = n_rows get no weight).
+  auto compute = [&](int t, const char* ks, int n_rows) {
+    if constexpr (kGather)
+      tile_step<true, false>(w, L, qf, ks, ks + kTileBytes, 32 * t, n_rows, c2);
+    else
+      tile_step<false, false>(w, L, qf, ks, ks + kTileBytes, 0, 0, c2);
+  };
 
-  // ---- phase 1: the persistent blocks, every tile shared by all 8 waves.
-  // Wave w moves key rows 4 w .. 4 w + 3 of each tile (one K and one V
-  // instruction), as in the dense kernel.
-  const int n_pt = n_p * NWB;
+  // ---- phase 1: the persistent blocks, every tile shared by all waves.
+  const int np_rows = n_p * B;
+  const int n_pt = (np_rows + 31) / 32;
   auto issue_p = [&](int t, char* ks) {
-    t = __builtin_amdgcn_readfirstlane(min(t, n_pt - 1));
-    const int blk = __builtin_amdgcn_readfirstlane(s_plist[t / NWB]);
-    const int r = 4 * wave + (lane >> 4);
-    const int64_t base = (int64_t)(blk * B + (t % NWB) * 32) * row_bytes;
-    const uint32_t off = (uint32_t)r * row_bytes;
-    __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
-                                     (lds_void*)(ks + wave * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
-                                     (lds_void*)(ks + kTileBytes + wave * 1024), 16, 0, 0);
+    issue_list<B, kPI>(kg, vg, row_bytes, s_plist, n_p, t, ks, wave, NW, lane);
   };
   if (n_pt > 0) {
+    L.lim = np_rows;
     issue_p(0, sS0);
     issue_p(1, sS1);
     issue_p(2, sS2);
     auto step = [&](int t, int u) {
-      tile_ready<4>();
+      tile_ready<kPWait>();
       issue_p(t + 3, stage((u + 3) & 3));
-      tile_step<false, false>(w, L, qf, stage(u), stage(u) + kTileBytes, 0, 0, c2);
+      compute(t, stage(u), np_rows);
     };
     int t = 0;
     for (; t + 4 <= n_pt; t += 4) {
@@ -375,35 +455,24 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
   // all blocks stepping together.
   int n_it = 0;
 #pragma unroll
-  for (int jj = 0; jj < G; ++jj) n_it = max(n_it, n_l[jj] * NWB);
+  for (int jj = 0; jj < G; ++jj) n_it = max(n_it, (n_l[jj] * B + 31) / 32);
   auto local_phase = [&](auto jc) {
     constexpr int J = decltype(jc)::value;
-    const int my = n_l[J] * NWB;
-    const int* list = s_llist[J];
+    const int nl_rows = n_l[J] * B;
+    const int my = (nl_rows + 31) / 32;
     auto issue_l = [&](int t, char* ks) {
-      t = __builtin_amdgcn_readfirstlane(min(t, my - 1));
-      const int blk = __builtin_amdgcn_readfirstlane(list[t / NWB]);
-      const int64_t base = (int64_t)(blk * B + (t % NWB) * 32) * row_bytes;
-#pragma unroll
-      for (int jj = 0; jj < 8 / NWB; ++jj) {
-        const int i = wq + NWB * jj;
-        const int r = 4 * i + (lane >> 4);
-        const uint32_t off = (uint32_t)r * row_bytes;
-        __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
-                                         (lds_void*)(ks + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
-                                         (lds_void*)(ks + kTileBytes + i * 1024), 16, 0, 0);
-      }
+      issue_list<B, kLI>(kg, vg, row_bytes, s_llist[J], n_l[J], t, ks, wq, NWB, lane);
     };
     // This block's my tiles, then idle barriers up to the group's n_it, so
     // every wave passes the same number of barriers.
     if (my > 0) {
+      L.lim = nl_rows;
 #pragma unroll
       for (int u = 0; u < SL - 1; ++u) issue_l(u, stage(J * SL + u));
       auto step = [&](int t, int u) {
         tile_ready<kLWait>();
         issue_l(t + SL - 1, stage(J * SL + (u + SL - 1) % SL));
-        tile_step<false, false>(w, L, qf, stage(J * SL + u), stage(J * SL + u) + kTileBytes, 0, 0, c2);
+        compute(t, stage(J * SL + u), nl_rows);
       };
       int t = 0;
       for (; t + SL <= my; t += SL) {
@@ -424,16 +493,16 @@ __global__ __launch_bounds__(512, 1) void attn_sparse_grouped_kernel(SparseArgs 
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  if (qrow < a.q_tokens) store_row(w, og + (int64_t)qrow * rs, g);
+  if (brow < B && qrow < a.q_tokens) store_row(w, og + (int64_t)qrow * rs, g);
 }
 
-template <typename Tout, int NWB>
+template <typename Tout, int NW, int NWB, int B>
 hipError_t launch_grouped(const SparseArgs& a, hipStream_t s) {
-  constexpr int G = 8 / NWB;
+  constexpr int G = NW / NWB;
   const int n_groups = (a.n_qblocks + G - 1) / G;
   const int64_t total = (int64_t)n_groups * a.n_heads * a.batch;
-  hipLaunchKernelGGL((attn_sparse_grouped_kernel<Tout, NWB>), dim3((uint32_t)total), dim3(512), 0,
-                     s, a, n_groups);
+  hipLaunchKernelGGL((attn_sparse_grouped_kernel<Tout, NW, NWB, B>), dim3((uint32_t)total),
+                     dim3(64 * NW), 0, s, a, n_groups);
   return hipGetLastError();
 }
 
@@ -449,9 +518,10 @@ template <typename Tout>
 hipError_t launch_t(const SparseArgs& a, hipStream_t s) {
   switch (a.block_tokens) {
     case 32: return launch_nw<Tout, 1, 2>(a, s);
-    case 64: return launch_grouped<Tout, 2>(a, s);
-    case 128: return launch_grouped<Tout, 4>(a, s);
-    default: return launch_grouped<Tout, 8>(a, s);
+    case 48: return launch_grouped<Tout, 4, 2, 48>(a, s);
+    case 64: return launch_grouped<Tout, 8, 2, 64>(a, s);
+    case 128: return launch_grouped<Tout, 8, 4, 128>(a, s);
+    default: return launch_grouped<Tout, 8, 8, 256>(a, s);
   }
 }
 

@@ -485,8 +485,10 @@ rcc_status rcc_block_sparse_attn(
   if (in_dtype != RCC_BF16 || !valid_dtype(out_dtype))
     return fail(RCC_ERR_DTYPE, "block-sparse attention takes bf16 inputs");
   if (head_dim != 128) return fail(RCC_ERR_SHAPE, "head_dim must be 128 (got %d)", head_dim);
-  if (block_tokens != 32 && block_tokens != 64 && block_tokens != 128 && block_tokens != 256)
-    return fail(RCC_ERR_SHAPE, "block_tokens must be 32, 64, 128 or 256 (got %d)", block_tokens);
+  if (block_tokens != 32 && block_tokens != 48 && block_tokens != 64 && block_tokens != 128 &&
+      block_tokens != 256)
+    return fail(RCC_ERR_SHAPE, "block_tokens must be 32, 48, 64, 128 or 256 (got %d)",
+                block_tokens);
   if (batch <= 0 || batch > 65535) return fail(RCC_ERR_SHAPE, "batch must be in [1, 65535]");
   if (n_heads <= 0 || n_heads > 65535) return fail(RCC_ERR_SHAPE, "n_heads must be in [1, 65535]");
   if (q_tokens < 0 || kv_tokens < 0 || n_persist < 0 || n_local < 0)

@@ -1,6 +1,6 @@
-"""Run one workload of the hot path a few times, for rocprofv3 collection.
+"""Run workloads of the hot path a few times each, for rocprofv3 collection.
 
-    python -m rope_chunk_causal_amd.prof_run WORKLOAD [--reps N]
+    python -m rope_chunk_causal_amd.prof_run WORKLOAD [WORKLOAD ...] [--reps N]
 
 WORKLOAD: attn_480p (chunk_causal_attn, 4680 queries over 14040 keys, 12
 heads), attn_720p (10800 over 75600, 40 heads), rope_480p (one 4680-token
@@ -10,10 +10,12 @@ the same two token sets), ring_1min (one layer of a 1-minute rollout, 80
 chunks x 4 steps, RoPE + ring write then attention over a 21-frame rolling
 window), sparse_sf512 (block_sparse_attn on the Sparse Forcing-shaped
 memory at Top-K 25, 12.5 and 6.25 %, then the dense kernel over the same
-memory), copy (a plain 1 GiB device-to-device copy: the
-reference for scaling HBM byte counters), all (every one of them: copy,
-then the others in the order listed).  Inputs are seeded
-N(0,1) bf16 on the device; nothing is checked here (the tests do that).
+memory), sparse_sf344 (the same with [3,4,4] blocks of 48 tokens), copy (a
+plain 1 GiB device-to-device copy: the reference for scaling HBM byte
+counters), all (copy, attn_480p, attn_720p, rope_480p, rope_sp_b64,
+qkv_480p, qkv_sp_b64, sparse_sf512, in that order).  Workloads run in the
+order given.  Inputs are seeded N(0,1) bf16 on the device; nothing is
+checked here (the tests do that).
 """
 from __future__ import annotations
 
@@ -110,14 +112,14 @@ def ring_1min(reps: int, gen) -> None:
                 rcc.chunk_causal_attn_ring(g, ring, qo, kc, vc, out, 1 / math.sqrt(D))
 
 
-def sparse_sf512(reps: int, gen) -> None:
+def sparse_sf512(reps: int, gen, workloads=None) -> None:
     w0 = next(iter(synth.SPARSE_WORKLOADS.values()))
     q = _randn(gen, 1, w0.q_tokens, w0.n_heads, w0.head_dim)
     k = _randn(gen, 1, w0.kv_tokens, w0.n_heads, w0.head_dim)
     v = _randn(gen, 1, w0.kv_tokens, w0.n_heads, w0.head_dim)
     o = torch.empty_like(q)
     scale = 1 / math.sqrt(w0.head_dim)
-    for w in synth.SPARSE_WORKLOADS.values():
+    for w in (workloads or synth.SPARSE_WORKLOADS).values():
         p, l = synth.block_lists(w, 7)
         dp, dl = torch.from_numpy(p).cuda(), torch.from_numpy(l).cuda()
         for _ in range(reps):
@@ -136,17 +138,19 @@ def copy(reps: int) -> None:
 
 def main() -> None:
     p = argparse.ArgumentParser()
-    p.add_argument("workload", choices=["attn_480p", "attn_720p", "rope_480p", "rope_sp_b64",
+    p.add_argument("workload", nargs="+", choices=["attn_480p", "attn_720p", "rope_480p", "rope_sp_b64",
                                         "qkv_480p", "qkv_sp_b64", "ring_1min", "sparse_sf512",
+                                        "sparse_sf344",
                                         "copy", "all"])
     p.add_argument("--reps", type=int, default=3)
     a = p.parse_args()
     rcc.lib()
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
-    names = ["copy", "attn_480p", "attn_720p", "rope_480p", "rope_sp_b64", "qkv_480p",
-             "qkv_sp_b64", "sparse_sf512"] \
-        if a.workload == "all" else [a.workload]
+    names = []
+    for n in a.workload:
+        names += ["copy", "attn_480p", "attn_720p", "rope_480p", "rope_sp_b64", "qkv_480p",
+                  "qkv_sp_b64", "sparse_sf512"] if n == "all" else [n]
     for n in names:
         if n == "copy":
             copy(a.reps)
@@ -158,6 +162,8 @@ def main() -> None:
             ring_1min(a.reps, gen)
         elif n == "sparse_sf512":
             sparse_sf512(a.reps, gen)
+        elif n == "sparse_sf344":
+            sparse_sf512(a.reps, gen, synth.SPARSE_WORKLOADS_344)
         else:
             rope(n, a.reps, gen)
         torch.cuda.synchronize()

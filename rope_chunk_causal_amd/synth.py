@@ -257,3 +257,14 @@ def seed_for(workload: str, start_frame: int, step: int, tensor: str) -> int:
             "480p_rolling_1min": 900}[workload]
     t = {"q": 0, "k": 100000, "v": 200000, "kc": 300000, "vc": 400000}[tensor]
     return base + 10 * start_frame + step + t
+
+# The same memory with Sparse Forcing's [3,4,4] blocks (48 tokens: three
+# latent frames of 4 x 4 patches, 112 blocks per 3-frame chunk at 896x512):
+# query chunk 112 blocks, local window 12 frames (448 blocks), persistent
+# memory 6 frames' worth (224 blocks); Top-K of 25%, 12.5% and 6.25% of the
+# window.  The keys and queries are the [1,8,8] workloads' counts (5376 and
+# 32256 tokens).
+SPARSE_WORKLOADS_344: Dict[str, SparseWorkload] = {
+    name: SparseWorkload(name, 12, 128, 48, 112, 224, 448, k)
+    for name, k in (("sf344_top25", 112), ("sf344_top12.5", 56), ("sf344_top6.25", 28))
+}

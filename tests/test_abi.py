@@ -298,7 +298,8 @@ def test_ring_positions_and_attention_host_checks():
     (dict(in_dtype=rcc.RCC_F32), rcc.RCC_ERR_DTYPE),
     (dict(out_dtype=5), rcc.RCC_ERR_DTYPE),
     (dict(head_dim=64), rcc.RCC_ERR_SHAPE),
-    (dict(block=48), rcc.RCC_ERR_SHAPE),
+    (dict(block=40), rcc.RCC_ERR_SHAPE),
+    (dict(block=96), rcc.RCC_ERR_SHAPE),
     (dict(block=512), rcc.RCC_ERR_SHAPE),
     (dict(n_p=600, n_l=425), rcc.RCC_ERR_SHAPE),             # more than 1024 entries
     (dict(kv=32768 * 32 + 32, cache=1 << 21, block=32), rcc.RCC_ERR_SHAPE),  # > 32768 blocks

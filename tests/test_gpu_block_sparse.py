@@ -57,6 +57,9 @@ def _run(B, nh, n_q, kv, cap, blk, n_p, n_l, seed, out_dtype="bf16", lists=None)
     (1, 1, 512, 2560, 2560, 256, 3, 2, "bf16"),
     (1, 2, 128, 4096, 4096, 64, 0, 9, "bf16"),   # local lists only
     (1, 2, 128, 4096, 4096, 64, 7, 0, "bf16"),   # persistent list only
+    (1, 2, 150, 960, 1000, 48, 2, 3, "bf16"),    # [3,4,4] blocks of 48; ragged last query block
+    (2, 3, 96, 1440, 1440, 48, 4, 6, "f32"),     # 48-row blocks, two batch entries
+    (1, 2, 480, 4800, 4800, 48, 0, 9, "bf16"),   # 48-row blocks, local lists only, 10 blocks
 ])
 def test_small_shapes_every_row(B, nh, n_q, kv, cap, blk, n_p, n_l, out_dtype):
     out, (qb, kb, vb), (persist, local) = _run(B, nh, n_q, kv, cap, blk, n_p, n_l, 31, out_dtype)
@@ -69,9 +72,10 @@ def test_small_shapes_every_row(B, nh, n_q, kv, cap, blk, n_p, n_l, out_dtype):
     check_attn(got, ref, f"sparse B{B} q{n_q} kv{kv} blk{blk}")
 
 
-def test_every_block_selected_matches_the_dense_kernel():
+@pytest.mark.parametrize("blk", [64, 48])
+def test_every_block_selected_matches_the_dense_kernel(blk):
     t = torch()
-    nh, n_q, kv, blk = 2, 256, 2048, 64
+    nh, n_q, kv = 2, 4 * blk, 32 * blk
     n_kb = kv // blk
     persist = np.tile(np.arange(0, n_kb, 2, dtype=np.int32), (1, nh, 1))
     local = np.tile(np.arange(1, n_kb, 2, dtype=np.int32), (1, nh, n_q // blk, 1))
@@ -112,12 +116,13 @@ def test_list_order_and_padding_do_not_change_bits():
     assert bool((a.view(t.int16) == b.view(t.int16)).all())
 
 
-@pytest.mark.parametrize("name", sorted(synth.SPARSE_WORKLOADS))
+@pytest.mark.parametrize("name", sorted(synth.SPARSE_WORKLOADS) + sorted(synth.SPARSE_WORKLOADS_344))
 def test_sparse_forcing_shapes_every_row(name):
-    """Sparse Forcing-shaped memory (84 query blocks of 64 tokens, 168
-    persistent + 336 window blocks, 12 heads): every query row of every head,
-    and the whole NaN-poisoned output finite."""
-    w = synth.SPARSE_WORKLOADS[name]
+    """Sparse Forcing-shaped memory, 12 heads: [1,8,8] blocks (84 query blocks
+    of 64 tokens, 168 persistent + 336 window blocks) and [3,4,4] blocks (112
+    query blocks of 48 tokens, 224 persistent + 448 window blocks).  Every
+    query row of every head, and the whole NaN-poisoned output finite."""
+    w = {**synth.SPARSE_WORKLOADS, **synth.SPARSE_WORKLOADS_344}[name]
     persist, local = synth.block_lists(w, 7)
     out, (qb, kb, vb), _ = _run(w.batch, w.n_heads, w.q_tokens, w.kv_tokens, w.kv_tokens, w.block,
                                 0, 0, 71, lists=(persist, local))
@@ -134,7 +139,7 @@ def test_errors_reported_without_launch():
     kc = t.zeros((1, 256, 2, 128), dtype=t.bfloat16, device="cuda")
     out = t.full_like(q, 3.0)
     lists = t.zeros((1, 2, 1, 2), dtype=t.int32, device="cuda")
-    for kw, status in ((dict(block_tokens=48), rcc.RCC_ERR_SHAPE),
+    for kw, status in ((dict(block_tokens=40), rcc.RCC_ERR_SHAPE),
                        (dict(kv_tokens=257), rcc.RCC_ERR_RANGE)):
         a = dict(kv_tokens=256, block_tokens=64)
         a.update(kw)

@@ -71,18 +71,21 @@ def test_dense_attention_cache_past_4gib(big):
     assert bool((out[:, :, 1:NH - 1] == 0).all())
 
 
-def test_block_sparse_cache_past_4gib(big):
+@pytest.mark.parametrize("blk", [64, 48])
+def test_block_sparse_cache_past_4gib(big, blk):
+    """Blocks of 64 (a tile inside one block) and of 48 (tiles that span two
+    blocks; block ROWS_4G // 48 itself straddles the 4 GiB line)."""
     t = torch()
-    blk = 64
-    far = ROWS_4G // blk                     # first block past 4 GiB
+    far = ROWS_4G // blk                     # the block holding the first row past 4 GiB
     n_kb = CAP // blk
+    n_qb = -(-NQ // blk)
     persist = np.array([far, far + 4, 17], dtype=np.int32)
-    local = np.array([[n_kb - 1, far + 14, n_kb + 5, -1], [far + 2, 3, n_kb - 1, n_kb - 1]],
-                     dtype=np.int32)
+    local = np.array([[n_kb - 1, far + 14, n_kb + 5, -1], [far + 2, 3, n_kb - 1, n_kb - 1],
+                      [far + 1, 0, far + 3, -1]], dtype=np.int32)[:n_qb]
     P = np.broadcast_to(persist, (B, NH, 3)).copy()
-    Lc = np.broadcast_to(local, (B, NH, 2, 4)).copy()
+    Lc = np.broadcast_to(local, (B, NH, n_qb, 4)).copy()
     out = t.full((B, NQ, NH, D), float("nan"), dtype=t.bfloat16, device="cuda")
-    say("block-sparse, blocks past 4 GiB", CAP)
+    say("block-sparse, blocks past 4 GiB", CAP, "block", blk)
     rcc.block_sparse_attn(big["dq"], big["dk"], big["dv"], out, CAP, blk, t.from_numpy(P).cuda(),
                           t.from_numpy(Lc).cuda(), 1.0 / math.sqrt(D))
     t.cuda.synchronize()
