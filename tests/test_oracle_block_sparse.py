@@ -50,10 +50,16 @@ def _brute(q, kc, vc, kv, blk, persist, local, scale):
     return out
 
 
-def test_brute_force_tiny():
-    B, nh, d, blk, n_q, kv = 2, 2, 4, 4, 10, 24          # 3 query blocks (last short), 6 key blocks
+@pytest.mark.parametrize("blk,n_q,kv", [
+    (4, 10, 24),     # 3 query blocks (last short), 6 key blocks
+    (3, 8, 20),      # blocks of an odd size (as 48 = 3 x 16): 3 query blocks, 6 key blocks + 2 rows
+    (6, 13, 30),     # 3 query blocks (last of 1 row), 5 key blocks
+])
+def test_brute_force_tiny(blk, n_q, kv):
+    B, nh, d = 2, 2, 4
+    n_qb, n_kb = -(-n_q // blk), kv // blk
     q, kc, vc = _rand((B, n_q, nh, d), 1), _rand((B, kv + 3, nh, d), 2), _rand((B, kv + 3, nh, d), 3)
-    persist, local = _lists(4, B, nh, 3, 6, 2, 3)
+    persist, local = _lists(4, B, nh, n_qb, n_kb, 2, 3)
     got = S.block_sparse_attention(q, kc, vc, kv, blk, persist, local, 0.4)
     np.testing.assert_allclose(got, _brute(q, kc, vc, kv, blk, persist, local, 0.4),
                                rtol=0, atol=1e-12)
