@@ -198,7 +198,8 @@ RING_PINS = [
 ]
 
 SPARSE_PINS = [
-    (TS.test_brute_force_tiny, ()),
+    (TS.test_brute_force_tiny, (4, 10, 24)),
+    (TS.test_brute_force_tiny, (3, 8, 20)),
     (TS.test_every_block_selected_is_dense_attention, ()),
     (TS.test_identical_keys_average_v_and_empty_gives_zero, ()),
     (TS.test_padding_repeats_and_order_change_nothing, ()),
