@@ -21,7 +21,9 @@
  * - Arguments are checked on the host before anything is launched; a call
  *   that returns anything but RCC_OK has launched nothing and written
  *   nothing.  Launches are asynchronous on `stream` (0 = the null stream);
- *   a failed launch returns RCC_ERR_HIP.  No call synchronises the host.
+ *   a failed launch returns RCC_ERR_HIP.  Sizes whose launch grid would
+ *   exceed 2^32 work-items return RCC_ERR_SHAPE without launching.  No call
+ *   synchronises the host.
  * - rcc_last_error() returns a human-readable detail of the last non-OK
  *   status returned on the calling thread.
  */

@@ -177,6 +177,7 @@ bool attn_d128_supported(const AttnArgs& a, rcc_dtype in) {
 hipError_t launch_attn_d128(const AttnArgs& a, rcc_dtype out, hipStream_t s) {
   const int n_qt = (a.q_tokens + kBM - 1) / kBM;
   const int64_t total = (int64_t)n_qt * a.n_heads * a.batch;
+  if (!grid_fits(total, kThreads)) return hipErrorInvalidConfiguration;
   if (out == RCC_BF16)
     hipLaunchKernelGGL((attn_d128_kernel<__bf16>), dim3((uint32_t)total), dim3(kThreads), 0, s, a, n_qt);
   else

@@ -501,6 +501,7 @@ hipError_t launch_grouped(const SparseArgs& a, hipStream_t s) {
   constexpr int G = NW / NWB;
   const int n_groups = (a.n_qblocks + G - 1) / G;
   const int64_t total = (int64_t)n_groups * a.n_heads * a.batch;
+  if (!grid_fits(total, 64 * NW)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_sparse_grouped_kernel<Tout, NW, NWB, B>), dim3((uint32_t)total),
                      dim3(64 * NW), 0, s, a, n_groups);
   return hipGetLastError();
@@ -509,6 +510,7 @@ hipError_t launch_grouped(const SparseArgs& a, hipStream_t s) {
 template <typename Tout, int NW, int S>
 hipError_t launch_nw(const SparseArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.n_qblocks * a.n_heads * a.batch;
+  if (!grid_fits(total, 64 * NW)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_sparse_kernel<Tout, NW, S>), dim3((uint32_t)total), dim3(64 * NW), 0,
                      s, a);
   return hipGetLastError();

@@ -317,6 +317,7 @@ int feature_group(int n_ft) { return n_ft < kGroupTiles ? n_ft : kGroupTiles; }
 template <int BT>
 hipError_t launch_bt(const QkvArgs& a, int n_ft, int64_t n_tok, hipStream_t s) {
   const int64_t n_tt = (n_tok + BT - 1) / BT;
+  if (!grid_fits(n_ft * n_tt, kThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(qkv_rope_kernel<BT>, dim3((uint32_t)(n_ft * n_tt)), dim3(kThreads), 0, s, a,
                      n_ft, (int)n_tt, feature_group(n_ft));
   return hipGetLastError();

@@ -22,6 +22,10 @@ rcc_status fail(rcc_status st, const char* fmt, ...) {
 
 rcc_status from_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return RCC_OK;
+  // The launchers' own refusal of a grid beyond 32-bit work-item counts
+  // (nothing launched): the sizes are too large for one call.
+  if (e == hipErrorInvalidConfiguration)
+    return fail(RCC_ERR_SHAPE, "%s: the launch grid would exceed 2^32 work-items", what);
   return fail(RCC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 

@@ -8,6 +8,14 @@
 
 namespace rcc {
 
+// A one-dimensional dispatch carries groups * threads work-items in 32 bits.
+// Launchers refuse larger grids with hipErrorInvalidConfiguration instead of
+// letting the cast to the launch's grid size truncate them (which would
+// leave outputs unwritten).
+inline bool grid_fits(int64_t groups, int threads) {
+  return groups * threads <= (int64_t)UINT32_MAX;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -116,7 +124,7 @@ hipError_t launch_attn_d128(const AttnArgs& a, rcc_dtype out, hipStream_t s);
 // (attn_sparse.hip; bf16, head_dim 128).
 struct SparseArgs {
   int32_t batch, n_heads;
-  int32_t q_tokens, kv_tokens, block_tokens;  // block_tokens in {32, 64, 128, 256}
+  int32_t q_tokens, kv_tokens, block_tokens;  // block_tokens in {32, 48, 64, 128, 256}
   int32_t n_qblocks, n_kblocks;               // ceil(q_tokens / B), kv_tokens / B
   int32_t n_persist, n_local;                 // list lengths
   int64_t cache_tokens;

@@ -73,6 +73,10 @@ def _sealed(cfg, buf=FAKE, floats=None):
     (dict(q_tokens=-1), rcc.RCC_ERR_SHAPE),
     (dict(scale=0.0), rcc.RCC_ERR_SHAPE),
     (dict(scale=-0.1), rcc.RCC_ERR_SHAPE),
+    # valid sizes whose bf16 / head_dim-128 launch would exceed 2^32 work-items
+    (dict(in_dtype=rcc.RCC_BF16, out_dtype=rcc.RCC_BF16, head_dim=128, batch=65535,
+          n_heads=65535, q_tokens=512, q_pos=0, kv_tokens=512, chunk_tokens=512, cache=512),
+     rcc.RCC_ERR_SHAPE),
 ])
 def test_attn_host_checks(kw, status):
     a = dict(in_dtype=rcc.RCC_F32, out_dtype=rcc.RCC_F32, batch=1, n_heads=2, head_dim=24,
@@ -310,6 +314,10 @@ def test_ring_positions_and_attention_host_checks():
     (dict(local=FAKE + 2), rcc.RCC_ERR_ALIGN),
     (dict(out=FAKE + 8), rcc.RCC_ERR_ALIGN),
     (dict(q_tokens=0, q=0), rcc.RCC_OK),                     # nothing to do
+    # valid sizes whose launch grid would exceed 2^32 work-items
+    (dict(batch=1024, nh=1024, q_tokens=1024 * 256, block=256, n_p=0, n_l=0), rcc.RCC_ERR_SHAPE),
+    (dict(batch=1024, nh=1024, q_tokens=1024 * 48, kv=960, block=48, n_p=0, n_l=0),
+     rcc.RCC_ERR_SHAPE),
 ])
 def test_block_sparse_host_checks(kw, status):
     a = dict(in_dtype=rcc.RCC_BF16, out_dtype=rcc.RCC_BF16, batch=1, nh=2, head_dim=128,
