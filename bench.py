@@ -214,22 +214,8 @@ def main():
     sp_bytes = 6.0 * B_sp * n_sp * nh * D * 2
     sp_gbps = sp_bytes / (sp_ms * 1e-3) / 1e9
     del sp_sets
-    # Reference: a plain device-to-device copy (torch copy_) moving the same
-    # bytes (half read, half written), two rotating buffer pairs.
-    n_el = int(sp_bytes // 4)
-    cp = [(torch.empty(n_el, device=dev, dtype=bf), torch.empty(n_el, device=dev, dtype=bf))
-          for _ in range(2)]
-    for i in range(3):
-        cp[i % 2][1].copy_(cp[i % 2][0])
-    cp_ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    cp_ev[0].record()
-    for i in range(reps):
-        cp[i % 2][1].copy_(cp[i % 2][0])
-        cp_ev[i + 1].record()
-    torch.cuda.synchronize()
-    cp_ms = sum(cp_ev[i].elapsed_time(cp_ev[i + 1]) for i in range(reps)) / reps
-    cp_gbps = 4.0 * n_el / (cp_ms * 1e-3) / 1e9
-    del cp
+    cp_gbps = _plain_copy_gbps(sp_bytes, reps, dev)
+    cp480_gbps = _plain_copy_gbps(rope_bytes, reps, dev)
 
     rollout = rollout_480p(rcc, synth, cfg, tables, randn, stream, dev)
     qkv = qkv_rope_fused(rcc, synth, cfg, tables, randn, stream, dev)
@@ -264,6 +250,9 @@ def main():
         "attn_tflops": round(attn_tflops, 2),
         "rope_ms": round(rope_ms, 4),
         "rope_gbps": round(rope_gbps, 1),
+        "rope_frac_hbm": round(rope_gbps / PEAK_HBM_GBPS, 4),
+        "rope_plain_copy_gbps": round(cp480_gbps, 1),
+        "rope_frac_of_plain_copy": round(rope_gbps / cp480_gbps, 4),
         "rope_sp_shard_b64": {"ms": round(sp_ms, 4), "gbps": round(sp_gbps, 1),
                               "bytes": sp_bytes, "frac_hbm": round(sp_gbps / PEAK_HBM_GBPS, 4),
                               "plain_copy_gbps": round(cp_gbps, 1),
@@ -287,6 +276,27 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows, wl, s, kv, scale)
         result["cpu_oracle_other_workloads"] = cpu_oracle_workloads()
     print(json.dumps(result), flush=True)
+
+
+def _plain_copy_gbps(nbytes, reps, dev):
+    """A plain device-to-device copy (torch copy_) moving the same bytes (half
+    read, half written), two rotating buffer pairs, HIP events per copy: the
+    rate a bandwidth-bound kernel of this size can be held against."""
+    import torch
+    n_el = int(nbytes // 4)
+    bf = torch.bfloat16
+    cp = [(torch.empty(n_el, device=dev, dtype=bf), torch.empty(n_el, device=dev, dtype=bf))
+          for _ in range(2)]
+    for i in range(3):
+        cp[i % 2][1].copy_(cp[i % 2][0])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        cp[i % 2][1].copy_(cp[i % 2][0])
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps
+    return 4.0 * n_el / (ms * 1e-3) / 1e9
 
 
 def _time_events(fn, stream, reps):
