@@ -310,8 +310,9 @@ __device__ __forceinline__ void issue_list(const char* kg, const char* vg, uint3
 // idles at the barriers.
 //
 // Blocks of 48 rows ([SF]'s [3,4,4]) run 4-wave workgroups of two query
-// blocks (64 KB of stages, two workgroups per CU; 112 blocks per head make
-// 1344 of them at 12 heads, so finer work evens out the last round), and
+// blocks (64 KB of stages, two workgroups per CU: a 12-head chunk of 112
+// blocks per head is 672 of them over 512 slots, a smaller last round than
+// 336 eight-wave workgroups over 256), and
 // read each list as a key stream of 32-row tiles across block boundaries:
 // three tiles per two blocks, only a list's last tile partial and masked.  A
 // block's second wave holds its rows 32 .. 47; its other 16 rows are
