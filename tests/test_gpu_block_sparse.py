@@ -91,18 +91,20 @@ def test_every_block_selected_matches_the_dense_kernel(blk):
                max_abs=4e-3, mean_abs=4e-4, rel_l2=1e-2)
 
 
-def test_empty_selection_gives_zeros():
+@pytest.mark.parametrize("blk", [64, 48])
+def test_empty_selection_gives_zeros(blk):
     t = torch()
     persist = np.full((1, 2, 3), -1, dtype=np.int32)
     local = np.array([[[[99, -1]], [[4, 5]]]], dtype=np.int32).reshape(1, 2, 1, 2)
-    out, _, _ = _run(1, 2, 64, 320, 320, 64, 0, 0, 51, lists=(persist, local))
+    out, _, _ = _run(1, 2, blk, 5 * blk, 5 * blk, blk, 0, 0, 51, lists=(persist, local))
     assert bool((out[:, :, 0] == 0).all())              # head 0: nothing valid
     assert bool(t.isfinite(out).all())
 
 
-def test_list_order_and_padding_do_not_change_bits():
+@pytest.mark.parametrize("blk", [64, 48])
+def test_list_order_and_padding_do_not_change_bits(blk):
     t = torch()
-    B, nh, n_q, kv, blk = 1, 2, 192, 1536, 64
+    B, nh, n_q, kv = 1, 2, 3 * blk, 24 * blk
     g = np.random.Generator(np.random.PCG64(61))
     persist = g.choice(24, size=(B, nh, 4), replace=False).astype(np.int32)
     local = np.stack([np.stack([g.choice(24, 5, replace=False) for _ in range(3)])
