@@ -2,7 +2,8 @@
 caller's stream) replays to the same bits as the eager calls.
 
 The step is rope3d_apply_append then chunk_causal_attn on a 480P-shaped
-chunk (smaller grid, same head shape).  The graph is replayed several times
+chunk (smaller grid, same head shape); a second graph holds the fused QKV
+projection and block-sparse attention with 64- and 48-row blocks.  The graph is replayed several times
 with eager work and synchronisations between replays, and every replay's
 q', cache and attention output are compared with the eager result bit for
 bit.  The library records no memset or allocation, so replays need nothing
@@ -62,4 +63,66 @@ def test_graph_replays_match_eager_bitwise():
         graph.replay()
         t.cuda.synchronize()
         for got, ref in ((qo, e_qo), (kc, e_kc), (vc, e_vc), (out, e_out)):
+            assert bool((got.view(i16) == ref.view(i16)).all()), r
+
+
+def test_graph_of_fused_qkv_and_block_sparse_replays_bitwise():
+    """The fused QKV projection writing q' and the cache, then block-sparse
+    attention of q' over the cache with [1,8,8]-sized (64) and [3,4,4]-sized
+    (48) blocks, captured together; replays match the eager calls bit for
+    bit."""
+    t = torch()
+    import numpy as np
+    F, H, W, s, nh, D, K = 2, 8, 16, 2, 2, 128, 256
+    L, hw = F * H * W, H * W
+    cfg = rcc.rope_cfg(44, 42, 42, 16, 16, 16)
+    tables = rcc.rope3d_tables(cfg)
+    g = rcc.grid(F, H, W, s, 0)
+    x = to_dev(synth.normal((1, L, K), 120, "bf16"), "bf16")
+    wq = (to_dev(synth.normal((3 * nh * D, K), 121, "bf16"), "bf16").float() /
+          math.sqrt(K)).to(t.bfloat16)
+    cap = (s + F) * hw
+    kc0 = to_dev(synth.normal((1, cap, nh, D), 122, "bf16"), "bf16")
+    vc0 = to_dev(synth.normal((1, cap, nh, D), 123, "bf16"), "bf16")
+    lists = {}
+    gen = np.random.Generator(np.random.PCG64(124))
+    for blk in (64, 48):
+        n_qb, n_kb = -(-L // blk), cap // blk
+        p = gen.choice(n_kb, size=(1, nh, 2), replace=False).astype(np.int32)
+        loc = gen.integers(-1, n_kb, size=(1, nh, n_qb, 3)).astype(np.int32)
+        lists[blk] = (t.from_numpy(p).cuda(), t.from_numpy(loc).cuda())
+    scale = 1.0 / math.sqrt(D)
+
+    def step(kc, vc, qo, outs):
+        rcc.qkv_rope_append(tables, g, x, wq, None, qo, kc, vc)
+        for blk, o in zip((64, 48), outs):
+            rcc.block_sparse_attn(qo, kc, vc, o, cap, blk, *lists[blk], scale)
+
+    say("graph (qkv + block-sparse): eager reference")
+    e_kc, e_vc, e_qo = kc0.clone(), vc0.clone(), t.empty(1, L, nh, D, device="cuda",
+                                                        dtype=t.bfloat16)
+    e_outs = [t.empty_like(e_qo) for _ in range(2)]
+    step(e_kc, e_vc, e_qo, e_outs)
+    t.cuda.synchronize()
+    assert all(bool(t.isfinite(o).all()) for o in e_outs)
+
+    kc, vc, qo = kc0.clone(), vc0.clone(), t.empty_like(e_qo)
+    outs = [t.empty_like(e_qo) for _ in range(2)]
+    graph = t.cuda.CUDAGraph()
+    say("graph (qkv + block-sparse): capture")
+    with t.cuda.graph(graph):
+        step(kc, vc, qo, outs)
+    t.cuda.synchronize()
+    i16 = t.int16
+    for r in range(3):
+        for y in [qo] + outs:
+            y.fill_(float("nan"))
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        step(kc0.clone(), vc0.clone(), t.empty_like(e_qo), [t.empty_like(e_qo) for _ in range(2)])
+        t.cuda.synchronize()
+        say("graph (qkv + block-sparse): replay", r)
+        graph.replay()
+        t.cuda.synchronize()
+        for got, ref in [(qo, e_qo), (kc, e_kc), (vc, e_vc)] + list(zip(outs, e_outs)):
             assert bool((got.view(i16) == ref.view(i16)).all()), r
