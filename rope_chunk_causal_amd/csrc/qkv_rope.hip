@@ -219,6 +219,10 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
   // token's 256 B, 4 tokens per instruction.  A wave reads back only what it
   // wrote, and its LDS operations complete in order: no barrier.
   char* tile = stage(wave >> 2) + (wave & 3) * 8192;
+  // Cache row of each of the wave's 32 tokens of the current block, written
+  // by the lane that owns the token and read back by the lanes storing it
+  // (a wave's LDS operations complete in order).
+  __shared__ int64_t sRow[kWaves][32];
   const float2* tab = reinterpret_cast<const float2*>(a.tables);
   const int c = lane & 15;
   const int fc = f0 + wf * 128 + c * 8;
@@ -230,7 +234,15 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int m = min(t0 + wt * 32 * TB + tb * 32 + l32, n_tok - 1);
-    const TokenPos pos = token_position(a.grid, m - (m / a.n_tokens) * a.n_tokens);
+    const int mb = m / a.n_tokens;
+    const TokenPos pos = token_position(a.grid, m - mb * a.n_tokens);
+    // This lane's token's cache row (the store phase takes it from the lane
+    // that owns the token instead of recomputing the position), and the
+    // float2 index shift of each band's row for the table lookups.
+    if (g == 0) sRow[wave][l32] = (int64_t)mb * a.cache_tokens + pos.row;
+    const int sh_t = pos.t * a.pt;
+    const int sh_h = (int)a.off_h + pos.h * a.ph - a.pt;
+    const int sh_w = (int)a.off_w + pos.w * a.pw - a.pt - a.ph;
     // Per 32-feature block, the cos/sin of its 8 rotary pairs for the lane's
     // token are all loaded before any is used.
 #pragma unroll
@@ -250,15 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int pr = ((d0 + j4 * 8 + g * 4) >> 1) + e;  // rotary pair inside the head
-            const float2* src;
-            if (pr < a.pt) {
-              src = tab + (int64_t)pos.t * a.pt + pr;
-            } else if (pr < a.pt + a.ph) {
-              src = tab + a.off_h + (int64_t)pos.h * a.ph + (pr - a.pt);
-            } else {
-              src = tab + a.off_w + (int64_t)pos.w * a.pw + (pr - a.pt - a.ph);
-            }
-            cs[j4][e] = *src;
+            cs[j4][e] = tab[pr + (pr < a.pt ? sh_t : pr < a.pt + a.ph ? sh_h : sh_w)];
           }
       }
 #pragma unroll
@@ -292,13 +296,11 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
         const int tl = it * 4 + (lane >> 4);
         const int mm = t0 + wt * 32 * TB + tb * 32 + tl;
         if (mm >= n_tok) break;
-        const int b = mm / a.n_tokens;
-        const int i = mm - b * a.n_tokens;
         int64_t row;
         if (which_c == 0) {
-          row = (int64_t)b * a.n_tokens + i;
+          row = mm;
         } else {
-          row = (int64_t)b * a.cache_tokens + token_position(a.grid, i).row;
+          row = sRow[wave][tl];
         }
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(tile + tl * 256 + ((c ^ (tl & 15)) << 4));
         *reinterpret_cast<bf16x8*>(obase + row * hd + dcol) = v;

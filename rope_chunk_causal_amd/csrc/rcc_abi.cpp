@@ -33,6 +33,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(rcc_dtype d) { return d == RCC_F32 || d == RCC_BF16; }
 constexpr int64_t kI32Max = 2147483647;
 
+int64_t table_floats(const rcc_rope3d_cfg& c) {
+  return (int64_t)c.max_t * c.d_t + (int64_t)c.max_h * c.d_h + (int64_t)c.max_w * c.d_w;
+}
+
 rcc_status check_cfg(const rcc_rope3d_cfg* c) {
   if (!c) return fail(RCC_ERR_NULL, "cfg is NULL");
   if (c->d_t <= 0 || c->d_h <= 0 || c->d_w <= 0 || (c->d_t | c->d_h | c->d_w) & 1)
@@ -42,11 +46,11 @@ rcc_status check_cfg(const rcc_rope3d_cfg* c) {
     return fail(RCC_ERR_SHAPE, "table lengths must be positive");
   if (!(c->theta > 0.0) || !isfinite(c->theta))
     return fail(RCC_ERR_SHAPE, "theta must be positive and finite");
+  // Kernels index the tables with 32-bit offsets.
+  if (table_floats(*c) > kI32Max)
+    return fail(RCC_ERR_SHAPE, "tables of %lld floats; at most 2^31 - 1",
+                (long long)table_floats(*c));
   return RCC_OK;
-}
-
-int64_t table_floats(const rcc_rope3d_cfg& c) {
-  return (int64_t)c.max_t * c.d_t + (int64_t)c.max_h * c.d_h + (int64_t)c.max_w * c.d_w;
 }
 
 // FNV-1a over the descriptor's fields (not its padding bytes): a descriptor
