@@ -111,6 +111,11 @@ rcc_status check_grid(const rcc_grid* g, int64_t n_tokens, rcc::GridArgs* out) {
   out->block_h = 0;
   out->block_w = 0;
   out->blocks_w = 0;
+  out->div_hw = rcc::make_fastdiv((uint32_t)hw);
+  out->div_w = rcc::make_fastdiv((uint32_t)g->width);
+  out->div_window = rcc::make_fastdiv(1);
+  out->div_bh = rcc::make_fastdiv(1);
+  out->div_bw = rcc::make_fastdiv(1);
   return RCC_OK;
 }
 
@@ -132,9 +137,12 @@ rcc_status check_ring(const rcc_grid* g, const rcc_ring* r, rcc::GridArgs* out,
     out->block_h = r->block_h;
     out->block_w = r->block_w;
     out->blocks_w = g->width / r->block_w;
+    out->div_bh = rcc::make_fastdiv((uint32_t)r->block_h);
+    out->div_bw = rcc::make_fastdiv((uint32_t)r->block_w);
   }
   out->sink = r->sink_frames;
   out->window = r->window_frames;
+  out->div_window = rcc::make_fastdiv((uint32_t)r->window_frames);
   *ring_rows = rows;
   return RCC_OK;
 }
@@ -208,6 +216,8 @@ rcc_status rope_append(const rcc_rope3d_tables* tables, const rcc_grid* grid,
     return fail(RCC_ERR_DTYPE, "in-place q_out needs in_dtype == out_dtype");
 
   rcc::RopeArgs a;
+  a.div_row_chunks = rcc::make_fastdiv((uint32_t)(n_heads * (D / 8)));
+  a.div_slots = rcc::make_fastdiv((uint32_t)(D / 8));
   a.tables = tables_dev;
   a.pt = cfg->d_t / 2;
   a.ph = cfg->d_h / 2;

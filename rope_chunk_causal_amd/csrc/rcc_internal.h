@@ -16,6 +16,24 @@ inline bool grid_fits(int64_t groups, int threads) {
   return groups * threads <= (int64_t)UINT32_MAX;
 }
 
+// Division by a divisor fixed for a launch (Granlund and Montgomery,
+// "Division by Invariant Integers using Multiplication", PLDI 1994): with
+// l = ceil(log2 d) and m = ceil(2^(32+l) / d) - 2^32, the quotient of any
+// n < 2^31 by d is (mulhi(n, m) + n) >> l (the sum stays below 2^32).  The
+// host makes it; kernels divide with one multiply-high, an add and a shift.
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {  // d >= 1
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << (32 + l)) + d - 1) / d;
+  return FastDiv{(uint32_t)(m - (1ull << 32)), l};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -33,6 +51,9 @@ struct GridArgs {
   int32_t sink, window;       // ring layout (window 0 = no ring)
   int32_t block_h, block_w;   // blockified frames (0 = row-major)
   int32_t blocks_w;           // W / block_w
+  FastDiv div_hw, div_w;      // by H*W and by W
+  FastDiv div_window;         // by window (ring), by block_h and block_w
+  FastDiv div_bh, div_bw;     //   (blockified frames); divisor 1 when unused
 };
 
 struct TokenPos {
@@ -47,19 +68,21 @@ struct TokenPos {
 // plus the token's row-major index inside its block.
 __device__ __forceinline__ TokenPos token_position(const GridArgs& g, int32_t i) {
   const uint32_t ig = (uint32_t)(g.token_offset + i);
-  const uint32_t f = ig / (uint32_t)g.hw;
+  const uint32_t f = fdiv(ig, g.div_hw);
   const uint32_t rem = ig - f * (uint32_t)g.hw;
-  const uint32_t h = rem / (uint32_t)g.width;
+  const uint32_t h = fdiv(rem, g.div_w);
   TokenPos p;
   p.t = g.start_frame + (int32_t)f;
   p.h = (int32_t)h;
   p.w = (int32_t)(rem - h * (uint32_t)g.width);
   int32_t slot = p.t;
-  if (g.window > 0 && p.t >= g.sink)
-    slot = g.sink + (int32_t)((uint32_t)(p.t - g.sink) % (uint32_t)g.window);
+  if (g.window > 0 && p.t >= g.sink) {
+    const uint32_t x = (uint32_t)(p.t - g.sink);
+    slot = g.sink + (int32_t)(x - fdiv(x, g.div_window) * (uint32_t)g.window);
+  }
   uint32_t frow = rem;
   if (g.block_h > 0) {
-    const uint32_t hb = h / (uint32_t)g.block_h, wb = (uint32_t)p.w / (uint32_t)g.block_w;
+    const uint32_t hb = fdiv(h, g.div_bh), wb = fdiv((uint32_t)p.w, g.div_bw);
     const uint32_t dh = h - hb * (uint32_t)g.block_h, dw = (uint32_t)p.w - wb * (uint32_t)g.block_w;
     frow = ((hb * (uint32_t)g.blocks_w + wb) * (uint32_t)g.block_h + dh) * (uint32_t)g.block_w + dw;
   }
@@ -72,6 +95,7 @@ hipError_t launch_rope3d_tables(const rcc_rope3d_cfg& cfg, float* tables, hipStr
 hipError_t launch_rope3d_positions(const GridArgs& g, int32_t n, int32_t* thw, hipStream_t s);
 
 struct RopeArgs {
+  FastDiv div_row_chunks, div_slots;  // by n_heads * head_dim / 8 and by head_dim / 8
   const float* tables;
   int32_t pt, ph, pw;         // pairs per band
   int64_t off_h, off_w;       // float2 offsets of the h and w tables

@@ -148,9 +148,9 @@ __global__ __launch_bounds__(kBlock) void rope3d_apply_append_kernel(RopeArgs a)
   const uint32_t row_chunks = (uint32_t)a.n_heads * slots;
   const uint32_t tid = blockIdx.x * kBlock + threadIdx.x;
   if (tid >= (uint32_t)a.n_tokens * row_chunks) return;
-  const int32_t i = (int32_t)(tid / row_chunks);
+  const int32_t i = (int32_t)fdiv(tid, a.div_row_chunks);
   const uint32_t chunk = tid - (uint32_t)i * row_chunks;
-  const int32_t c = (int32_t)(chunk % slots);
+  const int32_t c = (int32_t)(chunk - fdiv(chunk, a.div_slots) * slots);
   const int32_t b = blockIdx.z;
   const TokenPos p = token_position(a.grid, i);
   const float2* tab = reinterpret_cast<const float2*>(a.tables);
