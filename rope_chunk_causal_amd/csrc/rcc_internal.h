@@ -30,8 +30,8 @@ inline FastDiv make_fastdiv(uint32_t d) {  // d >= 1
   const uint64_t m = ((1ull << (32 + l)) + d - 1) / d;
   return FastDiv{(uint32_t)(m - (1ull << 32)), l};
 }
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
-  return (__umulhi(n, f.m) + n) >> f.s;
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return ((uint32_t)(((uint64_t)n * f.m) >> 32) + n) >> f.s;
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
