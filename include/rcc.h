@@ -86,7 +86,7 @@ typedef struct {
 
 /*
  * Number of floats of the device table buffer for `cfg`, or -1 if cfg is
- * NULL or invalid (including tables of 2^31 floats or more).  Layout (float2 = {cos, sin}):
+ * NULL or invalid (including tables of more than 2^30 floats, 4 GiB).  Layout (float2 = {cos, sin}):
  *   [max_t][d_t/2] float2, then [max_h][d_h/2] float2, then [max_w][d_w/2].
  */
 RCC_API int64_t rcc_rope3d_tables_floats(const rcc_rope3d_cfg* cfg);
@@ -114,7 +114,7 @@ typedef struct {
  * rope3d_tables_init — host only, launches nothing: check `cfg` and the
  * buffer and write the sealed descriptor `*out`.
  * Errors: NULL (cfg, buf_dev or out); SHAPE (odd or non-positive band dim,
- * non-positive table length, tables of 2^31 floats or more, theta not
+ * non-positive table length, tables of more than 2^30 floats, theta not
  * positive and finite, buf_floats < rcc_rope3d_tables_floats(cfg)); ALIGN
  * (buf_dev not 16-byte aligned).
  * On error *out is zeroed (an unsealed descriptor).

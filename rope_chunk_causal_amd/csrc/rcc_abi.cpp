@@ -46,9 +46,9 @@ rcc_status check_cfg(const rcc_rope3d_cfg* c) {
     return fail(RCC_ERR_SHAPE, "table lengths must be positive");
   if (!(c->theta > 0.0) || !isfinite(c->theta))
     return fail(RCC_ERR_SHAPE, "theta must be positive and finite");
-  // Kernels index the tables with 32-bit offsets.
-  if (table_floats(*c) > kI32Max)
-    return fail(RCC_ERR_SHAPE, "tables of %lld floats; at most 2^31 - 1",
+  // Kernels address the tables with 32-bit byte offsets.
+  if (table_floats(*c) > (int64_t)1 << 30)
+    return fail(RCC_ERR_SHAPE, "tables of %lld floats; at most 2^30 (4 GiB)",
                 (long long)table_floats(*c));
   return RCC_OK;
 }

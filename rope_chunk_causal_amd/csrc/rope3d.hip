@@ -153,20 +153,16 @@ __global__ __launch_bounds__(kBlock) void rope3d_apply_append_kernel(RopeArgs a)
   const int32_t c = (int32_t)(chunk - fdiv(chunk, a.div_slots) * slots);
   const int32_t b = blockIdx.z;
   const TokenPos p = token_position(a.grid, i);
-  const float2* tab = reinterpret_cast<const float2*>(a.tables);
+  const char* tab = reinterpret_cast<const char*>(a.tables);
+  const int32_t sh_t = p.t * a.pt;
+  const int32_t sh_h = (int32_t)a.off_h + p.h * a.ph - a.pt;
+  const int32_t sh_w = (int32_t)a.off_w + p.w * a.pw - a.pt - a.ph;
   float cs[4], sn[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const int32_t j = 4 * c + qq;
-    const float2* src;
-    if (j < a.pt) {
-      src = tab + (int64_t)p.t * a.pt + j;
-    } else if (j < a.pt + a.ph) {
-      src = tab + a.off_h + (int64_t)p.h * a.ph + (j - a.pt);
-    } else {
-      src = tab + a.off_w + (int64_t)p.w * a.pw + (j - a.pt - a.ph);
-    }
-    const float2 v = *src;
+    const uint32_t idx = (uint32_t)(j + (j < a.pt ? sh_t : j < a.pt + a.ph ? sh_h : sh_w));
+    const float2 v = *reinterpret_cast<const float2*>(tab + idx * 8u);
     cs[qq] = v.x;
     sn[qq] = v.y;
   }

@@ -136,14 +136,14 @@ def test_positions_and_tables_host_checks():
         rcc.RCC_ERR_NULL
     assert L.rcc_rope3d_tables_init(ctypes.byref(good), FAKE, 1 << 20, None) == rcc.RCC_ERR_NULL
     assert L.rcc_rope3d_tables_build(None, None) == rcc.RCC_ERR_NULL
-    # tables of 2^31 floats or more (kernels index them with 32-bit offsets)
+    # tables of more than 2^30 floats (kernels address them with 32-bit byte offsets)
     huge = rcc.rope_cfg(44, 42, 42, 1 << 26, 64, 128)
     assert L.rcc_rope3d_tables_floats(ctypes.byref(huge)) == -1
     assert L.rcc_rope3d_tables_init(ctypes.byref(huge), FAKE, 1 << 40, ctypes.byref(desc)) == \
         rcc.RCC_ERR_SHAPE
-    edge = rcc.rope_cfg(2, 2, 2, (1 << 30) - 3, 1, 1)             # 2^31 - 2 floats: allowed
-    assert L.rcc_rope3d_tables_floats(ctypes.byref(edge)) == (1 << 31) - 2
-    over = rcc.rope_cfg(2, 2, 2, (1 << 30) - 2, 1, 1)             # 2^31 floats: refused
+    edge = rcc.rope_cfg(2, 2, 2, (1 << 29) - 2, 1, 1)             # 2^30 floats: allowed
+    assert L.rcc_rope3d_tables_floats(ctypes.byref(edge)) == 1 << 30
+    over = rcc.rope_cfg(2, 2, 2, (1 << 29) - 1, 1, 1)             # 2^30 + 2 floats: refused
     assert L.rcc_rope3d_tables_floats(ctypes.byref(over)) == -1
 
 
