@@ -86,8 +86,9 @@ typedef struct {
 
 /*
  * Number of floats of the device table buffer for `cfg`, or -1 if cfg is
- * NULL or invalid (including tables of more than 2^30 floats, 4 GiB).  Layout (float2 = {cos, sin}):
- *   [max_t][d_t/2] float2, then [max_h][d_h/2] float2, then [max_w][d_w/2].
+ * NULL or invalid (including tables of more than 2^30 floats, 4 GiB).
+ * Layout (float2 = {cos, sin}): [max_t][d_t/2] float2, then
+ * [max_h][d_h/2] float2, then [max_w][d_w/2].
  */
 RCC_API int64_t rcc_rope3d_tables_floats(const rcc_rope3d_cfg* cfg);
 
