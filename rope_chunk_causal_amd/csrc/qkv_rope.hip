@@ -110,7 +110,10 @@ __device__ __forceinline__ void stage_ready() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BT>
+// kWan: head_dim 128 with rotary bands of 22 / 21 / 21 pairs (t / h / w);
+// each 32-feature block then starts at a known place in its head, so every
+// pair's band is a compile-time fact (up to the lane half).
+template <int BT, bool kWan>
 __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_ft, int n_tt,
                                                                int gf) {
   using T = Tile<BT>;
@@ -240,9 +243,10 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
     // that owns the token instead of recomputing the position), and the
     // float2 index shift of each band's row for the table lookups.
     if (g == 0) sRow[wave][l32] = (int64_t)mb * a.cache_tokens + pos.row;
-    const int sh_t = pos.t * a.pt;
-    const int sh_h = (int)a.off_h + pos.h * a.ph - a.pt;
-    const int sh_w = (int)a.off_w + pos.w * a.pw - a.pt - a.ph;
+    const int pt = kWan ? 22 : a.pt, ph = kWan ? 21 : a.ph, pw = kWan ? 21 : a.pw;
+    const int sh_t = pos.t * pt;
+    const int sh_h = (int)a.off_h + pos.h * ph - pt;
+    const int sh_w = (int)a.off_w + pos.w * pw - pt - ph;
     // Per 32-feature block, the cos/sin of its 8 rotary pairs for the lane's
     // token are all loaded before any is used.
 #pragma unroll
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
       const int f = f0 + wf * 128 + fb * 32;  // first feature of the block (wave-uniform)
       if (f >= n_feat) continue;
       const int which = f / hd;
-      const int d0 = (f - which * hd) % a.head_dim;
+      const int d0 = kWan ? fb * 32 : (f - which * hd) % a.head_dim;
       f32x4 bias[4];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4)
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int pr = ((d0 + j4 * 8 + g * 4) >> 1) + e;  // rotary pair inside the head
-            cs[j4][e] = tab[pr + (pr < a.pt ? sh_t : pr < a.pt + a.ph ? sh_h : sh_w)];
+            cs[j4][e] = tab[pr + (pr < pt ? sh_t : pr < pt + ph ? sh_h : sh_w)];
           }
       }
 #pragma unroll
@@ -320,8 +324,13 @@ template <int BT>
 hipError_t launch_bt(const QkvArgs& a, int n_ft, int64_t n_tok, hipStream_t s) {
   const int64_t n_tt = (n_tok + BT - 1) / BT;
   if (!grid_fits(n_ft * n_tt, kThreads)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(qkv_rope_kernel<BT>, dim3((uint32_t)(n_ft * n_tt)), dim3(kThreads), 0, s, a,
-                     n_ft, (int)n_tt, feature_group(n_ft));
+  const bool wan = a.head_dim == 128 && a.pt == 22 && a.ph == 21 && a.pw == 21;
+  if (wan)
+    hipLaunchKernelGGL((qkv_rope_kernel<BT, true>), dim3((uint32_t)(n_ft * n_tt)), dim3(kThreads),
+                       0, s, a, n_ft, (int)n_tt, feature_group(n_ft));
+  else
+    hipLaunchKernelGGL((qkv_rope_kernel<BT, false>), dim3((uint32_t)(n_ft * n_tt)), dim3(kThreads),
+                       0, s, a, n_ft, (int)n_tt, feature_group(n_ft));
   return hipGetLastError();
 }
 

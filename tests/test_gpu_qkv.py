@@ -69,6 +69,7 @@ def _run(B, n, nh, dims, K, F, H, W, s, off, mx, bias, seed, sample=None):
     (2, 300, 3, (44, 42, 42), 128, 3, 10, 12, 6, 50, True),    # head_dim 128, several tiles
     (1, 1, 1, (12, 10, 10), 32, 1, 1, 1, 0, 0, False),          # one token, one K step
     (1, 257, 4, (16, 8, 8), 160, 2, 16, 16, 0, 0, False),       # K not a multiple of 64
+    (1, 200, 3, (40, 44, 44), 128, 2, 10, 10, 3, 0, True),      # head_dim 128, other bands
 ])
 def test_small_shapes_every_token(B, n, nh, dims, K, F, H, W, s, off, bias):
     _run(B, n, nh, dims, K, F, H, W, s, off, (16, 16, 16), bias, seed=11)
