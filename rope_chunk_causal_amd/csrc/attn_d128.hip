@@ -19,6 +19,11 @@
 // * Workgroups are renumbered so each XCD (dispatch is round-robin over the
 //   8 XCDs) gets a contiguous range of (batch, head, query-tile) work: query
 //   tiles of one head run on one XCD and share its L2 for K/V.
+// * Only the first tile's softmax step is checked: it sets each row's
+//   reference, and the other tiles' steps make no test, so a tile's
+//   exponentials and O^T MFMAs run as one straight-line block.  Each row's
+//   sum then certifies the sweep; a workgroup with a row whose sum left
+//   [2^-20, 2^100] sweeps again with every step checked.
 #include <type_traits>
 
 #include "attn_tile.h"
@@ -123,48 +128,69 @@ __global__ __launch_bounds__(kThreads, 1) void attn_d128_kernel(AttnArgs a, int 
   load_q<true>(qf, qg, rs, qclamp, g, a.scale_log2);
 
   const Dma dma = dma_offsets(wave, lane);
-  issue_tile(kg, vg, row_bytes, 0, kv_end, dma, sK0, sV0, wave, lane);
-  issue_tile(kg, vg, row_bytes, kBN, kv_end, dma, sK1, sV1, wave, lane);
-  issue_tile(kg, vg, row_bytes, 2 * kBN, kv_end, dma, sK2, sV2, wave, lane);
+  auto prologue = [&]() {
+    issue_tile(kg, vg, row_bytes, 0, kv_end, dma, sK0, sV0, wave, lane);
+    issue_tile(kg, vg, row_bytes, kBN, kv_end, dma, sK1, sV1, wave, lane);
+    issue_tile(kg, vg, row_bytes, 2 * kBN, kv_end, dma, sK2, sV2, wave, lane);
+  };
+  prologue();
 
   Lane L;
   lane_setup(L, lane);
   L.lim = min(a.kv_tokens, ((a.q_pos + qclamp) / C + 1) * C);
 
   WaveState w;
-  wave_init<true>(w);
   const float c2 = a.scale_log2;
 
   // Tile t lives in stage t % 4; tiles t+1 and t+2 are in flight while it is
   // computed, and tile t+3 starts into the stage that tile t-1 used.  The
-  // loop is instantiated twice: with the tile work, and (for a wave with no
-  // query rows) DMA and barriers only, so neither copy branches per tile.
-  auto sweep = [&](auto work) {
-    auto step = [&](int t, const char* ks, const char* vs, char* kn, char* vn) {
+  // first tile sets each row's reference (a checked step); the others run
+  // unchecked (kChecked false) unless `checked`, the fallback sweep.  The
+  // loop is instantiated for each and, for a wave with no query rows, as DMA
+  // and barriers only, so no copy branches per tile.
+  auto sweep = [&](auto work, auto checked) {
+    wave_init<true>(w);
+    auto step = [&](auto first, int t, const char* ks, const char* vs, char* kn, char* vn) {
       tile_ready<4>();
       issue_tile(kg, vg, row_bytes, (t + 3) * kBN, kv_end, dma, kn, vn, wave, lane);
       if constexpr (decltype(work)::value)
-        tile_step<true, true>(w, L, qf, ks, vs, t * kBN, lim_lo, c2);
+        tile_step<true, true, decltype(first)::value || decltype(checked)::value>(
+            w, L, qf, ks, vs, t * kBN, lim_lo, c2);
     };
-    int t = 0;
+    const std::true_type head;
+    const std::false_type body;
+    if (n_tiles > 0) step(head, 0, sK0, sV0, sK3, sV3);
+    int t = 1;
     for (; t + kStages <= n_tiles; t += kStages) {
-      step(t, sK0, sV0, sK3, sV3);
-      step(t + 1, sK1, sV1, sK0, sV0);
-      step(t + 2, sK2, sV2, sK1, sV1);
-      step(t + 3, sK3, sV3, sK2, sV2);
+      step(body, t, sK1, sV1, sK0, sV0);
+      step(body, t + 1, sK2, sV2, sK1, sV1);
+      step(body, t + 2, sK3, sV3, sK2, sV2);
+      step(body, t + 3, sK0, sV0, sK3, sV3);
     }
-    if (t < n_tiles) step(t, sK0, sV0, sK3, sV3);
-    if (t + 1 < n_tiles) step(t + 1, sK1, sV1, sK0, sV0);
-    if (t + 2 < n_tiles) step(t + 2, sK2, sV2, sK1, sV1);
+    if (t < n_tiles) step(body, t, sK1, sV1, sK0, sV0);
+    if (t + 1 < n_tiles) step(body, t + 1, sK2, sV2, sK1, sV1);
+    if (t + 2 < n_tiles) step(body, t + 2, sK3, sV3, sK2, sV2);
+    // No load may still be writing this workgroup's LDS after the sweep.
+    __builtin_amdgcn_s_waitcnt(0);
+    finish_rows<true>(w);
   };
   if (has_rows)
-    sweep(std::true_type{});
+    sweep(std::true_type{}, std::false_type{});
   else
-    sweep(std::false_type{});
-  // No load may still be writing this workgroup's LDS when it exits.
-  __builtin_amdgcn_s_waitcnt(0);
+    sweep(std::false_type{}, std::false_type{});
 
-  finish_rows<true>(w);
+  // Certificate of the unchecked steps (row_certified); a workgroup with a
+  // row that fails sweeps again with every step checked (only for scores
+  // that rise far above the first tile's, or rows with almost no weight).
+  // Rows past q_tokens repeat the last row and decide like it.
+  if (__syncthreads_or(n_tiles > 0 && has_rows && !row_certified(w))) {
+    prologue();
+    if (has_rows)
+      sweep(std::true_type{}, std::true_type{});
+    else
+      sweep(std::false_type{}, std::true_type{});
+  }
+
   if (qrow < a.q_tokens) store_row(w, og + (int64_t)qrow * rs, g);
 }
 

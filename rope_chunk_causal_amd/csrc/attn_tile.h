@@ -91,6 +91,10 @@ __device__ __forceinline__ void tile_ready() {
 //   below 2^56 (finite in bf16 and in the fp32 sums), and the reference never
 //   exceeds the row max, so the row's largest probability is at least 1.  l_run is the lane's half
 //   of the row sum (its 16 keys of each tile); finish_rows adds the halves.
+//   A sweep may also run its steps past the first unchecked (kChecked
+//   false: the first tile's max stays the reference and no test is made)
+//   and certify each row at the end (row_certified), falling back to a
+//   checked sweep for the rows' workgroup when one fails.
 struct WaveState {
   f32x16 oacc[4];
   f32x16 negm;          // -m_run in every element (base-2 scheme only)
@@ -154,7 +158,11 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[8], const __bf16* qg, int64_
 // so the compiler does not order these LDS reads after the other stages' DMA
 // writes.  kMask: keys at or past L.lim get no weight (only tiles that reach
 // lim_lo test it).  kBase2: the score bookkeeping (see WaveState).
-template <bool kMask, bool kBase2>
+// kChecked = false (base-2 scheme only): the reference never moves and no
+// test is made, so the exponentials and the O^T MFMAs form one straight-line
+// block; the caller certifies the row afterwards (row_certified) and redoes
+// the sweep with checked steps if a row fails.
+template <bool kMask, bool kBase2, bool kChecked = true>
 __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf16x8 (&qf)[8],
                                           const char* ks, const char* vs, int j0, int lim_lo,
                                           float c2) {
@@ -206,7 +214,7 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
     // it is more than 48 above it, or if the row has no weight (to the
     // first finite max, so that uniformly very negative scores do not all
     // underflow).  Lanes l and l + 32 hold the same row and decide alike.
-    if (__ballot(!(rsum <= kSumCap) || w.l_run == 0.f)) {
+    if (kChecked && __ballot(!(rsum <= kSumCap) || w.l_run == 0.f)) {
       float mx = s0[0];
 #pragma unroll
       for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);
@@ -272,6 +280,17 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
 template <bool kBase2>
 __device__ __forceinline__ void finish_rows(WaveState& w) {
   if constexpr (kBase2) w.l_run = xhalf_sum(w.l_run);
+}
+
+// After a sweep whose steps past the first were unchecked (finish_rows done):
+// the row's result is the checked scheme's up to rounding when its sum lies
+// in [2^-20, 2^100].  Every probability is at most the sum, so none passed
+// 2^100 (finite in bf16 and in the fp32 sums and O^T); and the largest is at
+// least the sum over the number of keys (below 2^31), at least 2^-51, so a
+// probability that underflows (below 2^-126) is below 2^-75 of it.  NaN
+// and inf fail the test.
+__device__ __forceinline__ bool row_certified(const WaveState& w) {
+  return w.l_run >= 0x1p-20f && w.l_run <= 0x1p100f;
 }
 
 // O / l for the lane's query row (column of O^T), stored to orow.  A row that

@@ -147,6 +147,23 @@ def test_stress_scores_rise_then_jump_past_fp32_range():
     say("rise/jump", check_attn(got, ref, "rise then jump"))
 
 
+@pytest.mark.parametrize("jump", [60.0, 95.0, 120.0])
+def test_stress_late_scores_around_the_certificate_bound(jump):
+    """Three late keys whose base-2 scores sit about `jump` above the first
+    tile's (the per-query spread of the construction is some 15%).  The
+    kernel's reference comes from the first tile and later tiles are not
+    tested one by one: a row sum up to 2^100 is accepted as is, a larger one
+    sends the workgroup through a second, checked sweep.  60 stays below the
+    bound, 120 passes it in every row (some sums overflow to inf), 95 lands
+    on both sides; every row must match the oracle."""
+    shift = np.zeros(2048)
+    s = jump * math.sqrt(128) / (math.log2(math.e) * 6.0)
+    shift[1800], shift[1801], shift[2000] = s, s - 0.5, s - 1.0
+    got, ref = _directed_case(930 + int(jump), 6.0, shift)
+    assert np.isfinite(got).all()
+    say("late jump", jump, check_attn(got, ref, f"late jump {jump}"))
+
+
 def test_stress_all_scores_far_below_zero():
     """Every logit near -210 (base-2 scores near -300): each probability
     underflows to zero against the initial reference, so the reference must
