@@ -40,6 +40,11 @@
 //   exceed 4 GiB.
 // * Workgroups are numbered XCD-major: the query blocks of one head run on
 //   one XCD and share its L2.
+// * In the grouped kernels only a wave's first key tile takes the checked
+//   softmax step (it sets each row's reference); the other tiles take no
+//   tile max and no test, and each stored row's sum certifies the result at
+//   the end.  A workgroup with a row whose sum left [2^-20, 2^100] streams
+//   both phases again with every step checked, from the lists still in LDS.
 #include <type_traits>
 
 #include "attn_tile.h"
@@ -412,87 +417,116 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attn_sparse_grouped_
   Lane L;
   lane_setup(L, lane);
   WaveState w;
-  wave_init<false>(w);
   const float c2 = a.scale_log2;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
   // Tile t of a key stream of n_rows rows (only a 48-row block's stream has a
-  // partial last tile: keys at or past L.lim = n_rows get no weight).
-  auto compute = [&](int t, const char* ks, int n_rows) {
+  // partial last tile: keys at or past L.lim = n_rows get no weight).  chk:
+  // a checked softmax step (see tile_step's kChecked).
+  auto compute = [&](auto chk, int t, const char* ks, int n_rows) {
+    constexpr bool C = decltype(chk)::value;
     if constexpr (kGather)
-      tile_step<true, false>(w, L, qf, ks, ks + kTileBytes, 32 * t, n_rows, c2);
+      tile_step<true, false, C>(w, L, qf, ks, ks + kTileBytes, 32 * t, n_rows, c2);
     else
-      tile_step<false, false>(w, L, qf, ks, ks + kTileBytes, 0, 0, c2);
+      tile_step<false, false, C>(w, L, qf, ks, ks + kTileBytes, 0, 0, c2);
   };
+  const std::true_type checked;
 
-  // ---- phase 1: the persistent blocks, every tile shared by all waves.
   const int np_rows = n_p * B;
   const int n_pt = (np_rows + 31) / 32;
   auto issue_p = [&](int t, char* ks) {
     issue_list<B, kPI>(kg, vg, row_bytes, s_plist, n_p, t, ks, wave, NW, lane);
   };
-  if (n_pt > 0) {
-    L.lim = np_rows;
-    issue_p(0, sS0);
-    issue_p(1, sS1);
-    issue_p(2, sS2);
-    auto step = [&](int t, int u) {
-      tile_ready<kPWait>();
-      issue_p(t + 3, stage((u + 3) & 3));
-      compute(t, stage(u), np_rows);
-    };
-    int t = 0;
-    for (; t + 4 <= n_pt; t += 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) step(t + u, u);
-    }
-#pragma unroll
-    for (int u = 0; u < 3; ++u)
-      if (t + u < n_pt) step(t + u, u);
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  __syncthreads();  // every wave is done with the shared stages
-
-  // ---- phase 2: each query block's own local blocks, SL stages per block,
-  // all blocks stepping together.
   int n_it = 0;
 #pragma unroll
   for (int jj = 0; jj < G; ++jj) n_it = max(n_it, (n_l[jj] * B + 31) / 32);
-  auto local_phase = [&](auto jc) {
-    constexpr int J = decltype(jc)::value;
-    const int nl_rows = n_l[J] * B;
-    const int my = (nl_rows + 31) / 32;
-    auto issue_l = [&](int t, char* ks) {
-      issue_list<B, kLI>(kg, vg, row_bytes, s_llist[J], n_l[J], t, ks, wq, NWB, lane);
-    };
-    // This block's my tiles, then idle barriers up to the group's n_it, so
-    // every wave passes the same number of barriers.
-    if (my > 0) {
-      L.lim = nl_rows;
-#pragma unroll
-      for (int u = 0; u < SL - 1; ++u) issue_l(u, stage(J * SL + u));
-      auto step = [&](int t, int u) {
-        tile_ready<kLWait>();
-        issue_l(t + SL - 1, stage(J * SL + (u + SL - 1) % SL));
-        compute(t, stage(J * SL + u), nl_rows);
+
+  // Both phases.  The wave's first key tile (the persistent stream's first,
+  // or its block's first local tile when there is no persistent block) is a
+  // checked step that sets each row's reference; the others are checked
+  // only in the fallback sweep (all_checked).
+  auto sweep = [&](auto all_checked) {
+    const std::integral_constant<bool, decltype(all_checked)::value> rest;
+    wave_init<false>(w);
+    // ---- phase 1: the persistent blocks, every tile shared by all waves.
+    // Tile t lives in stage t % 4.
+    if (n_pt > 0) {
+      L.lim = np_rows;
+      issue_p(0, sS0);
+      issue_p(1, sS1);
+      issue_p(2, sS2);
+      auto step = [&](auto chk, int t, int u) {
+        tile_ready<kPWait>();
+        issue_p(t + 3, stage((u + 3) & 3));
+        compute(chk, t, stage(u), np_rows);
       };
-      int t = 0;
-      for (; t + SL <= my; t += SL) {
+      step(checked, 0, 0);
+      int t = 1;
+      for (; t + 4 <= n_pt; t += 4) {
 #pragma unroll
-        for (int u = 0; u < SL; ++u) step(t + u, u);
+        for (int u = 0; u < 4; ++u) step(rest, t + u, (1 + u) & 3);
       }
 #pragma unroll
-      for (int u = 0; u < SL - 1; ++u)
-        if (t + u < my) step(t + u, u);
+      for (int u = 0; u < 3; ++u)
+        if (t + u < n_pt) step(rest, t + u, (1 + u) & 3);
+      __builtin_amdgcn_s_waitcnt(0);
     }
-    for (int t = my; t < n_it; ++t) tile_ready<kLWait>();
+    __syncthreads();  // every wave is done with the shared stages
+
+    // ---- phase 2: each query block's own local blocks, SL stages per
+    // block (tile t in the block's stage t % SL), all blocks stepping
+    // together.
+    auto local_phase = [&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const int nl_rows = n_l[J] * B;
+      const int my = (nl_rows + 31) / 32;
+      auto issue_l = [&](int t, char* ks) {
+        issue_list<B, kLI>(kg, vg, row_bytes, s_llist[J], n_l[J], t, ks, wq, NWB, lane);
+      };
+      // This block's my tiles, then idle barriers up to the group's n_it, so
+      // every wave passes the same number of barriers.
+      if (my > 0) {
+        L.lim = nl_rows;
+#pragma unroll
+        for (int u = 0; u < SL - 1; ++u) issue_l(u, stage(J * SL + u));
+        auto step = [&](auto chk, int t, int u) {
+          tile_ready<kLWait>();
+          issue_l(t + SL - 1, stage(J * SL + (u + SL - 1) % SL));
+          compute(chk, t, stage(J * SL + u), nl_rows);
+        };
+        if (n_pt > 0)
+          step(rest, 0, 0);
+        else
+          step(checked, 0, 0);
+        int t = 1;
+        for (; t + SL <= my; t += SL) {
+#pragma unroll
+          for (int u = 0; u < SL; ++u) step(rest, t + u, (1 + u) % SL);
+        }
+#pragma unroll
+        for (int u = 0; u < SL - 1; ++u)
+          if (t + u < my) step(rest, t + u, (1 + u) % SL);
+      }
+      for (int t = my; t < n_it; ++t) tile_ready<kLWait>();
+    };
+    switch (jw) {
+      case 0: local_phase(std::integral_constant<int, 0>{}); break;
+      case 1: if constexpr (G > 1) local_phase(std::integral_constant<int, 1>{}); break;
+      case 2: if constexpr (G > 2) local_phase(std::integral_constant<int, 2>{}); break;
+      default: if constexpr (G > 3) local_phase(std::integral_constant<int, 3>{}); break;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
   };
-  switch (jw) {
-    case 0: local_phase(std::integral_constant<int, 0>{}); break;
-    case 1: if constexpr (G > 1) local_phase(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (G > 2) local_phase(std::integral_constant<int, 2>{}); break;
-    default: if constexpr (G > 3) local_phase(std::integral_constant<int, 3>{}); break;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
+  sweep(std::false_type{});
+
+  // Certificate of the unchecked steps (row_certified) for every stored row
+  // that saw a key; a workgroup with a row that fails sweeps again with
+  // every step checked.  The lists stay in LDS, so the setup is not redone.
+  int my_tiles = n_pt;
+#pragma unroll
+  for (int jj = 0; jj < G; ++jj)
+    if (jj == jw) my_tiles += (n_l[jj] * B + 31) / 32;
+  const bool stored = brow < B && qrow < a.q_tokens;
+  if (__syncthreads_or(stored && my_tiles > 0 && !row_certified(w))) sweep(checked);
 
   if (brow < B && qrow < a.q_tokens) store_row(w, og + (int64_t)qrow * rs, g);
 }

@@ -158,10 +158,10 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[8], const __bf16* qg, int64_
 // so the compiler does not order these LDS reads after the other stages' DMA
 // writes.  kMask: keys at or past L.lim get no weight (only tiles that reach
 // lim_lo test it).  kBase2: the score bookkeeping (see WaveState).
-// kChecked = false (base-2 scheme only): the reference never moves and no
-// test is made, so the exponentials and the O^T MFMAs form one straight-line
-// block; the caller certifies the row afterwards (row_certified) and redoes
-// the sweep with checked steps if a row fails.
+// kChecked = false: the reference never moves and no test is made (no tile
+// max in the classic scheme), so the exponentials and the O^T MFMAs form one
+// straight-line block; the caller certifies the row afterwards
+// (row_certified) and redoes the sweep with checked steps if a row fails.
 template <bool kMask, bool kBase2, bool kChecked = true>
 __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf16x8 (&qf)[8],
                                           const char* ks, const char* vs, int j0, int lim_lo,
@@ -243,21 +243,23 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
     for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)p[r];
     w.l_run += rsum;
   } else {
-    float mx = s0[0];
+    if constexpr (kChecked) {
+      float mx = s0[0];
 #pragma unroll
-    for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);  // v_max3_f32
-    mx = fmaxf(mx, s0[15]);
-    mx = xhalf_max(mx) * c2;
-    // Lazy rescale: move the reference max only when it would grow by > 2^8.
-    const float m_use = (mx - w.m_run > kLazy) ? mx : w.m_run;
-    if (__ballot(m_use != w.m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
-      w.l_run *= alpha;
+      for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s0[r]), s0[r + 1]);  // v_max3_f32
+      mx = fmaxf(mx, s0[15]);
+      mx = xhalf_max(mx) * c2;
+      // Lazy rescale: move the reference max only when it would grow by > 2^8.
+      const float m_use = (mx - w.m_run > kLazy) ? mx : w.m_run;
+      if (__ballot(m_use != w.m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
+        w.l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
-      w.m_run = m_use;
+          for (int r = 0; r < 16; ++r) w.oacc[dt][r] *= alpha;
+        w.m_run = m_use;
+      }
     }
     float rsum = 0.f;
 #pragma unroll
@@ -282,7 +284,8 @@ __device__ __forceinline__ void finish_rows(WaveState& w) {
   if constexpr (kBase2) w.l_run = xhalf_sum(w.l_run);
 }
 
-// After a sweep whose steps past the first were unchecked (finish_rows done):
+// After a sweep whose steps past the first were unchecked (the row's whole
+// sum in l_run: finish_rows done in the base-2 scheme):
 // the row's result is the checked scheme's up to rounding when its sum lies
 // in [2^-20, 2^100].  Every probability is at most the sum, so none passed
 // 2^100 (finite in bf16 and in the fp32 sums and O^T); and the largest is at

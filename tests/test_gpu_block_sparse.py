@@ -135,6 +135,44 @@ def test_sparse_forcing_shapes_every_row(name):
     say(name, check_attn(to_host_f64(out), ref, name))
 
 
+@pytest.mark.parametrize("blk,jump", [(64, 60.0), (64, 120.0), (48, 60.0), (48, 120.0)])
+def test_late_scores_around_the_certificate_bound(blk, jump):
+    """Keys of one late local block (last in the visit order) whose base-2
+    scores sit about `jump` above the rest, along a seeded direction u
+    (q = N(0,1) + 6 u, those keys N(0,1) + s u).  The kernel takes each row's
+    reference from its first tile and tests no later tile: a row sum up to
+    2^100 is accepted (60), a larger or infinite one (120) sends the
+    workgroup through a second, checked sweep.  Every row against the oracle."""
+    D, nh, n_q, kv = 128, 1, 2 * blk, 16 * blk
+    g = np.random.Generator(np.random.PCG64(81 + int(jump) + blk))
+    u = g.standard_normal(D)
+    u /= np.linalg.norm(u)
+    s = jump * math.sqrt(D) / (math.log2(math.e) * 6.0)
+    shift = np.zeros(kv)
+    shift[13 * blk + 3], shift[13 * blk + 5], shift[13 * blk + 9] = s, s - 0.5, s - 1.0
+    q = synth.bf16_bits_to_f32(synth.normal((1, n_q, nh, D), 82, "bf16")) + 6.0 * u
+    k = synth.bf16_bits_to_f32(synth.normal((1, kv, nh, D), 83, "bf16"))
+    k += shift[None, :, None, None] * u
+    qb = synth.f32_to_bf16_bits(q.astype(np.float32))
+    kb = synth.f32_to_bf16_bits(k.astype(np.float32))
+    vb = synth.normal((1, kv, nh, D), 84, "bf16")
+    persist = np.array([[[0, 2, 4]]], dtype=np.int32)
+    local = np.array([[[[13, 7, 10], [10, 13, 7]]]], dtype=np.int32)
+    t = torch()
+    out = t.full((1, n_q, nh, D), float("nan"), dtype=t.float32, device="cuda")
+    say("sparse late jump", blk, jump)
+    rcc.block_sparse_attn(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), out, kv, blk,
+                          t.from_numpy(persist).cuda(), t.from_numpy(local).cuda(),
+                          1.0 / math.sqrt(D))
+    t.cuda.synchronize()
+    got = to_host_f64(out)
+    assert np.isfinite(got).all()
+    ref = S.block_sparse_attention(synth.to_f64(qb, "bf16"), synth.to_f64(kb, "bf16"),
+                                   synth.to_f64(vb, "bf16"), kv, blk, persist, local,
+                                   1.0 / math.sqrt(D))
+    say("sparse late jump", blk, jump, check_attn(got, ref, f"sparse late jump {blk} {jump}"))
+
+
 def test_errors_reported_without_launch():
     t = torch()
     q = t.zeros((1, 64, 2, 128), dtype=t.bfloat16, device="cuda")
