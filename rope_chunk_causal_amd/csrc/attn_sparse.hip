@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * NW, NW > 1 ? 2 : 1) void attn_sparse_kernel(Sp
   WaveState w;
   wave_init<false>(w);
   const float c2 = a.scale_log2;
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t row_bytes = __builtin_amdgcn_readfirstlane((uint32_t)(rs * 2));
 
   if (n_tiles > 0) {
 #pragma unroll
@@ -275,10 +275,15 @@ __device__ __forceinline__ void issue_list(const char* kg, const char* vg, uint3
       const int i = i0 + di * j;
       const int r = 4 * i + (lane >> 4);
       const uint32_t off = (uint32_t)r * row_bytes;
-      __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
-                                       (lds_void*)(ks + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
-                                       (lds_void*)(ks + kTileBytes + i * 1024), 16, 0, 0);
+      uint32_t ok = off + k_chunk(r, lane & 15), ov = off + v_chunk(r, lane & 15);
+      // Keeps the compiler from folding the lane offsets into 64-bit lane
+      // pointers outside the tile loop, which turns each load's address into
+      // two 64-bit vector multiply-adds instead of a scalar base plus a
+      // 32-bit offset.  Emits no instruction.
+      asm volatile("" : "+v"(ok), "+v"(ov));
+      __builtin_amdgcn_global_load_lds(kg + base + ok, (lds_void*)(ks + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + base + ov, (lds_void*)(ks + kTileBytes + i * 1024), 16,
+                                       0, 0);
     }
   } else {
     static_assert(B > 32 && B < 64, "a tile spans at most two blocks");
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attn_sparse_grouped_
   lane_setup(L, lane);
   WaveState w;
   const float c2 = a.scale_log2;
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t row_bytes = __builtin_amdgcn_readfirstlane((uint32_t)(rs * 2));
   // Tile t of a key stream of n_rows rows (only a 48-row block's stream has a
   // partial last tile: keys at or past L.lim = n_rows get no weight).  chk:
   // a checked softmax step (see tile_step's kChecked).
