@@ -22,8 +22,8 @@
 // * Only the first tile's softmax step is checked: it sets each row's
 //   reference, and the other tiles' steps make no test, so a tile's
 //   exponentials and O^T MFMAs run as one straight-line block.  Each row's
-//   sum then certifies the sweep; a workgroup with a row whose sum left
-//   [2^-20, 2^100] sweeps again with every step checked.
+//   sum and output then certify the sweep (row_certified); a workgroup with
+//   a row that fails sweeps again with every step checked.
 #include <type_traits>
 
 #include "attn_tile.h"

@@ -42,9 +42,10 @@
 //   one XCD and share its L2.
 // * In the grouped kernels only a wave's first key tile takes the checked
 //   softmax step (it sets each row's reference); the other tiles take no
-//   tile max and no test, and each stored row's sum certifies the result at
-//   the end.  A workgroup with a row whose sum left [2^-20, 2^100] streams
-//   both phases again with every step checked, from the lists still in LDS.
+//   tile max and no test, and each stored row's sum and output certify the
+//   result at the end (row_certified).  A workgroup with a row that fails
+//   streams both phases again with every step checked, from the lists still
+//   in LDS.
 #include <type_traits>
 
 #include "attn_tile.h"

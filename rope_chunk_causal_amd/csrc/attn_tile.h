@@ -285,15 +285,24 @@ __device__ __forceinline__ void finish_rows(WaveState& w) {
 }
 
 // After a sweep whose steps past the first were unchecked (the row's whole
-// sum in l_run: finish_rows done in the base-2 scheme):
-// the row's result is the checked scheme's up to rounding when its sum lies
-// in [2^-20, 2^100].  Every probability is at most the sum, so none passed
-// 2^100 (finite in bf16 and in the fp32 sums and O^T); and the largest is at
-// least the sum over the number of keys (below 2^31), at least 2^-51, so a
-// probability that underflows (below 2^-126) is below 2^-75 of it.  NaN
-// and inf fail the test.
+// sum in l_run: finish_rows done in the base-2 scheme): the row's result is
+// the checked scheme's up to rounding when its sum lies in [2^-20, 2^64] and
+// the lane's O^T accumulators are finite.  Every probability is at most the
+// sum, so none passed 2^64 (finite in bf16 and in the fp32 sums); the largest
+// is at least the sum over the number of keys (below 2^31), at least 2^-51,
+// so a probability that underflows (below 2^-126) is below 2^-75 of it; and
+// O^T, at most the sum times max |v|, overflows only for |v| past 2^64 (the
+// checked scheme lets the sum reach ~2^69), which the finiteness test
+// catches.  The tests compare bit patterns, so NaN and inf fail whatever
+// the compiler assumes about NaNs.
 __device__ __forceinline__ bool row_certified(const WaveState& w) {
-  return w.l_run >= 0x1p-20f && w.l_run <= 0x1p100f;
+  const uint32_t lb = __float_as_uint(w.l_run);
+  uint32_t e = 0;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e = max(e, __float_as_uint(w.oacc[dt][r]) & 0x7f800000u);
+  return lb >= 0x35800000u && lb <= 0x5f800000u && e != 0x7f800000u;  // 2^-20, 2^64
 }
 
 // O / l for the lane's query row (column of O^T), stored to orow.  A row that

@@ -147,14 +147,14 @@ def test_stress_scores_rise_then_jump_past_fp32_range():
     say("rise/jump", check_attn(got, ref, "rise then jump"))
 
 
-@pytest.mark.parametrize("jump", [60.0, 95.0, 120.0])
+@pytest.mark.parametrize("jump", [40.0, 66.0, 120.0])
 def test_stress_late_scores_around_the_certificate_bound(jump):
     """Three late keys whose base-2 scores sit about `jump` above the first
     tile's (the per-query spread of the construction is some 15%).  The
     kernel's reference comes from the first tile and later tiles are not
-    tested one by one: a row sum up to 2^100 is accepted as is, a larger one
-    sends the workgroup through a second, checked sweep.  60 stays below the
-    bound, 120 passes it in every row (some sums overflow to inf), 95 lands
+    tested one by one: a row sum up to 2^64 is accepted as is, a larger one
+    sends the workgroup through a second, checked sweep.  40 stays below the
+    bound, 120 passes it in every row (some sums overflow to inf), 66 lands
     on both sides; every row must match the oracle."""
     shift = np.zeros(2048)
     s = jump * math.sqrt(128) / (math.log2(math.e) * 6.0)
@@ -162,6 +162,46 @@ def test_stress_late_scores_around_the_certificate_bound(jump):
     got, ref = _directed_case(930 + int(jump), 6.0, shift)
     assert np.isfinite(got).all()
     say("late jump", jump, check_attn(got, ref, f"late jump {jump}"))
+
+
+def test_stress_unnormalised_output_past_fp32_range():
+    """Late keys 56-62 (base 2) above the first tile's scores, whose value
+    rows are 2^74: the row sums stay below 2^64 but the unnormalised O^T
+    (probabilities ~2^60 times 2^74) overflows fp32 in the unchecked sweep.
+    The output certificate must send the workgroup through the checked
+    sweep, which moves the reference and keeps O^T finite.  Outputs are
+    ~2^74, so the comparison is relative."""
+    t = torch()
+    lq, kv, d = 128, 2048, 128
+    g = np.random.Generator(np.random.PCG64(940))
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    sh = 60.0 * math.sqrt(d) / (math.log2(math.e) * 6.0)
+    shift = np.zeros(kv)
+    big = [1800, 1801, 2000]
+    shift[big] = [sh, sh - 0.5, sh - 1.0]
+    # small query noise, so every row's jump is 60 to within a few units
+    q = 0.1 * synth.bf16_bits_to_f32(synth.normal((1, lq, 1, d), 941, "bf16")) + 6.0 * u
+    k = synth.bf16_bits_to_f32(synth.normal((1, kv, 1, d), 942, "bf16"))
+    k += shift[None, :, None, None] * u
+    v = synth.bf16_bits_to_f32(synth.normal((1, kv, 1, d), 943, "bf16"))
+    v[0, big] *= 2.0 ** 74
+    qb = synth.f32_to_bf16_bits(q.astype(np.float32))
+    kb = synth.f32_to_bf16_bits(k.astype(np.float32))
+    vb = synth.f32_to_bf16_bits(v.astype(np.float32))
+    out = t.full((1, lq, 1, d), float("nan"), dtype=t.float32, device="cuda")
+    say("output overflow")
+    rcc.chunk_causal_attn(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), out,
+                          kv - lq, kv, kv, 1 / math.sqrt(d))
+    t.cuda.synchronize()
+    got = to_host_f64(out)
+    ref = A.chunk_causal_attention(synth.to_f64(qb, "bf16"), synth.to_f64(kb, "bf16"),
+                                   synth.to_f64(vb, "bf16"), kv - lq, kv, kv, 1 / math.sqrt(d))
+    assert np.isfinite(got).all()
+    scale = np.abs(ref).max(axis=-1, keepdims=True)
+    rel = np.abs(got - ref) / scale
+    say("output overflow rel err", float(rel.max()))
+    assert rel.max() < 2e-2
 
 
 def test_stress_all_scores_far_below_zero():
