@@ -173,6 +173,46 @@ def test_late_scores_around_the_certificate_bound(blk, jump):
     say("sparse late jump", blk, jump, check_attn(got, ref, f"sparse late jump {blk} {jump}"))
 
 
+@pytest.mark.parametrize("blk", [64, 48])
+def test_unnormalised_output_past_fp32_range(blk):
+    """A late local block whose keys sit ~60 (base 2) above the rest and
+    whose value rows are 2^74: row sums stay below 2^64 but the unnormalised
+    O^T overflows fp32 in the unchecked sweep, so the output certificate
+    must send the workgroup through the checked sweep.  Outputs are ~2^74,
+    so the comparison is relative."""
+    D, nh, n_q, kv = 128, 1, 2 * blk, 16 * blk
+    g = np.random.Generator(np.random.PCG64(91 + blk))
+    u = g.standard_normal(D)
+    u /= np.linalg.norm(u)
+    sh = 60.0 * math.sqrt(D) / (math.log2(math.e) * 6.0)
+    big = [13 * blk + 3, 13 * blk + 5, 13 * blk + 9]
+    shift = np.zeros(kv)
+    shift[big] = [sh, sh - 0.5, sh - 1.0]
+    q = 0.1 * synth.bf16_bits_to_f32(synth.normal((1, n_q, nh, D), 92, "bf16")) + 6.0 * u
+    k = synth.bf16_bits_to_f32(synth.normal((1, kv, nh, D), 93, "bf16"))
+    k += shift[None, :, None, None] * u
+    v = synth.bf16_bits_to_f32(synth.normal((1, kv, nh, D), 94, "bf16"))
+    v[0, big] *= 2.0 ** 74
+    qb, kb, vb = (synth.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    persist = np.array([[[0, 2, 4]]], dtype=np.int32)
+    local = np.array([[[[13, 7, 10], [10, 13, 7]]]], dtype=np.int32)
+    t = torch()
+    out = t.full((1, n_q, nh, D), float("nan"), dtype=t.float32, device="cuda")
+    say("sparse output overflow", blk)
+    rcc.block_sparse_attn(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), out, kv, blk,
+                          t.from_numpy(persist).cuda(), t.from_numpy(local).cuda(),
+                          1.0 / math.sqrt(D))
+    t.cuda.synchronize()
+    got = to_host_f64(out)
+    assert np.isfinite(got).all()
+    ref = S.block_sparse_attention(synth.to_f64(qb, "bf16"), synth.to_f64(kb, "bf16"),
+                                   synth.to_f64(vb, "bf16"), kv, blk, persist, local,
+                                   1.0 / math.sqrt(D))
+    rel = np.abs(got - ref) / np.abs(ref).max(axis=-1, keepdims=True)
+    say("sparse output overflow", blk, "rel err", float(rel.max()))
+    assert rel.max() < 2e-2
+
+
 def test_errors_reported_without_launch():
     t = torch()
     q = t.zeros((1, 64, 2, 128), dtype=t.bfloat16, device="cuda")
