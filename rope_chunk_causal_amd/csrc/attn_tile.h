@@ -11,9 +11,10 @@
 // of 4 keys x 64 B).  V^T operands come from ds_read_b64_tr_b16: in each
 // 16-lane group, lane i receives element i%4 of the 8-byte chunk addressed by
 // lane 4e + i/4, so 16 lanes that address a 4-key x 16-dim block get that
-// block transposed.  Lazy rescaling: a row's reference max moves only when
-// the tile max exceeds it by more than 2^8; P stays <= 256 and the final
-// O / l is exact.
+// block transposed.  Softmax bookkeeping (WaveState): a row's reference
+// moves only when its scores rise well above it (lazy rescaling), or, in
+// the sweeps the kernels run by default, only on the first tile, with the
+// row's sum and output certified at the end (row_certified).
 #pragma once
 
 #include "rcc_internal.h"
