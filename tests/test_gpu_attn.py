@@ -82,6 +82,22 @@ def test_ragged_and_masked_shapes(b, lq, nh, d, cap, q_pos, kv, C, in_dt, out_dt
     check_attn(got, ref, f"{(b, lq, nh, d, q_pos, kv, C)}")
 
 
+@pytest.mark.parametrize("kv", [1, 20, 32, 33, 64, 65, 96, 100, 128, 129, 160, 192, 200, 224,
+                                256, 257, 288])
+@pytest.mark.parametrize("C", [0, 16])
+def test_fast_path_every_tile_count(kv, C):
+    """bf16, head_dim 128 (the fast kernel): key ranges of 1 to 9 tiles of
+    32, so the first (checked) tile, the loop over groups of four tiles and
+    every remainder of the unchecked sweep are hit.  The queries are the
+    last min(kv, 40) keys' positions; C = 0 stands for one chunk over
+    everything, 16 makes the visibility block-causal inside the queries."""
+    lq = min(kv, 40)
+    chunk = lq if C == 0 else C
+    got, ref, _ = _attn_case(1, lq, 3, 128, kv, kv - lq, kv, chunk, "bf16", "bf16",
+                             700 + kv + C, label="tile count")
+    check_attn(got, ref, f"tile count kv={kv} C={chunk}")
+
+
 def test_stress_peaked_softmax():
     """Q scaled x8: sharply peaked rows exercise the running-max rescale."""
     got, ref, _ = _attn_case(1, 256, 2, 128, 2048, 1024, 2048, 1024, "bf16", "f32", 500,

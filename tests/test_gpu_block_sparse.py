@@ -213,6 +213,33 @@ def test_unnormalised_output_past_fp32_range(blk):
     assert rel.max() < 2e-2
 
 
+@pytest.mark.parametrize("blk", [64, 48])
+@pytest.mark.parametrize("n_sel", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("where", ["persist", "local"])
+def test_stream_lengths(blk, n_sel, where):
+    """Streams of 1 to 5 key blocks (2 to 10 tiles of 32 keys at 64-row
+    blocks, 2 to 8 at 48-row blocks, the last one partial for odd counts),
+    all in the persistent list or all in the local lists: the wave's first
+    (checked) tile, the unrolled tile loops and their remainders.  Every row
+    against the oracle."""
+    nh, n_q, kv = 2, 2 * blk + 7, 12 * blk
+    g = np.random.Generator(np.random.PCG64(500 + 10 * n_sel + blk))
+    n_qb, n_kb = -(-n_q // blk), kv // blk
+    if where == "persist":
+        persist = np.stack([g.choice(n_kb, n_sel, replace=False) for _ in range(nh)])[None]
+        local = np.zeros((1, nh, n_qb, 0), dtype=np.int32)
+    else:
+        persist = np.zeros((1, nh, 0), dtype=np.int32)
+        local = np.stack([np.stack([g.choice(n_kb, n_sel, replace=False) for _ in range(n_qb)])
+                          for _ in range(nh)])[None]
+    persist, local = persist.astype(np.int32), local.astype(np.int32)
+    out, (qb, kb, vb), _ = _run(1, nh, n_q, kv, kv, blk, 0, 0, 520 + n_sel, lists=(persist, local))
+    ref = S.block_sparse_attention(synth.to_f64(qb, "bf16"), synth.to_f64(kb, "bf16"),
+                                   synth.to_f64(vb, "bf16"), kv, blk, persist, local,
+                                   1.0 / math.sqrt(128))
+    check_attn(to_host_f64(out), ref, f"stream {where} {n_sel} x {blk}")
+
+
 def test_errors_reported_without_launch():
     t = torch()
     q = t.zeros((1, 64, 2, 128), dtype=t.bfloat16, device="cuda")
