@@ -3,7 +3,9 @@ caller's stream) replays to the same bits as the eager calls.
 
 The step is rope3d_apply_append then chunk_causal_attn on a 480P-shaped
 chunk (smaller grid, same head shape); a second graph holds the fused QKV
-projection and block-sparse attention with 64- and 48-row blocks.  The graph is replayed several times
+projection and block-sparse attention with 64- and 48-row blocks; a third,
+an attention launch whose unchecked sweep fails its certificate and sweeps
+again checked.  Each graph is replayed several times
 with eager work and synchronisations between replays, and every replay's
 q', cache and attention output are compared with the eager result bit for
 bit.  The library records no memset or allocation, so replays need nothing
@@ -126,3 +128,45 @@ def test_graph_of_fused_qkv_and_block_sparse_replays_bitwise():
         t.cuda.synchronize()
         for got, ref in [(qo, e_qo), (kc, e_kc), (vc, e_vc)] + list(zip(outs, e_outs)):
             assert bool((got.view(i16) == ref.view(i16)).all()), r
+
+
+def test_graph_replay_of_the_certificate_fallback():
+    """Dense attention on scores that jump past the fp32 exponent range late
+    in the key range: the unchecked sweep fails its certificate and every
+    workgroup sweeps again with every step checked.  Captured in a graph,
+    the launch (the decision and the second sweep included) replays to the
+    eager bits."""
+    t = torch()
+    import numpy as np
+    lq, kv, d = 256, 2048, 128
+    g = np.random.Generator(np.random.PCG64(130))
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = synth.bf16_bits_to_f32(synth.normal((1, lq, 2, d), 131, "bf16")) + 6.0 * u
+    k = synth.bf16_bits_to_f32(synth.normal((1, kv, 2, d), 132, "bf16"))
+    k[0, 1900:1903] += 400.0 * u
+    dq = to_dev(synth.f32_to_bf16_bits(q.astype(np.float32)), "bf16")
+    dk = to_dev(synth.f32_to_bf16_bits(k.astype(np.float32)), "bf16")
+    dv = to_dev(synth.normal((1, kv, 2, d), 133, "bf16"), "bf16")
+    scale = 1.0 / math.sqrt(d)
+    say("graph (certificate fallback): eager reference")
+    ref = t.empty_like(dq)
+    rcc.chunk_causal_attn(dq, dk, dv, ref, kv - lq, kv, kv, scale)
+    t.cuda.synchronize()
+    assert bool(t.isfinite(ref).all())
+    out = t.empty_like(dq)
+    graph = t.cuda.CUDAGraph()
+    say("graph (certificate fallback): capture")
+    with t.cuda.graph(graph):
+        rcc.chunk_causal_attn(dq, dk, dv, out, kv - lq, kv, kv, scale)
+    t.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        scratch = t.empty_like(dq)
+        rcc.chunk_causal_attn(dq, dk, dv, scratch, kv - lq, kv, kv, scale)
+        t.cuda.synchronize()
+        say("graph (certificate fallback): replay", r)
+        graph.replay()
+        t.cuda.synchronize()
+        assert bool((out.view(t.int16) == ref.view(t.int16)).all()), r
+
