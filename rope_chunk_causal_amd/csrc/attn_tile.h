@@ -330,13 +330,27 @@ __device__ __forceinline__ void store_row(const WaveState& w, Tout* orow, int g)
 
 // XCD-aware renumbering of a 1-D grid: dispatch is round-robin over the 8
 // XCDs, so consecutive ids of the result land on one XCD and share its L2.
+// XCD x receives the blocks x, x + 8, ...: per of them if x < rem (or rem is
+// 0), per - 1 otherwise.  Its ids form one contiguous range, and the ranges
+// are laid out in the XCD order 0, 4, 1, 5, 2, 6, 3, 7, so that where the
+// first rem XCDs hold one block more, each pair of neighbouring ranges holds
+// 2 per - 1 ids: for 19 query tiles x 12 heads (228 blocks, rem 4) every
+// range boundary then falls inside a head or on a head boundary such that
+// each XCD holds two heads, where the order 0, 1, ..., 7 left three XCDs
+// with parts of three heads.
 __device__ __forceinline__ int xcd_major_id() {
   const int total = (int)gridDim.x;
   const int bid = blockIdx.x;
   const int per = (total + kXcds - 1) / kXcds;
   const int rem = total % kXcds;
   const int xcd = bid % kXcds;
-  return xcd * per - (rem && xcd > rem ? xcd - rem : 0) + bid / kXcds;
+  const int pos = 2 * (xcd & 3) + (xcd >> 2);
+  int start = 0;
+#pragma unroll
+  for (int y = 0; y < kXcds; ++y) {
+    if (2 * (y & 3) + (y >> 2) < pos) start += (rem == 0 || y < rem) ? per : per - 1;
+  }
+  return start + bid / kXcds;
 }
 
 }  // namespace attn128
