@@ -35,7 +35,8 @@
 // * Epilogue, one 32-token block at a time: bias (staged in LDS once) and
 //   rotation in registers, bf16 results staged through the (then free) LDS
 //   ring so that 16 lanes write each token's 256 B of a wave's 128 features
-//   with one 16-byte store each.
+//   with one 16-byte store each.  The stores are non-temporal: the outputs
+//   are written once and not read again by this kernel.
 #include "rcc_internal.h"
 
 namespace rcc {
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_rope_kernel(QkvArgs a, int n_
           row = sRow[wave][tl];
         }
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(tile + tl * 256 + ((c ^ (tl & 15)) << 4));
-        *reinterpret_cast<bf16x8*>(obase + row * hd + dcol) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(obase + row * hd + dcol));
       }
     }
   }
