@@ -60,8 +60,8 @@ def _code_only(text: str) -> str:
 def kernel_source_hash() -> str:
     """Hash of what the attention kernels are compiled from (comments and
     whitespace ignored): their sources, and from the shared internal header
-    the vector typedefs and the attention argument struct (the rest of that
-    header serves other kernels)."""
+    the vector typedefs, the buffer-resource flags and the attention argument
+    struct (the rest of that header serves other kernels)."""
     import re
     csrc = os.path.join(ROOT, "rope_chunk_causal_amd", "csrc")
     h = hashlib.sha256()
@@ -69,7 +69,8 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, f)) as fh:
             h.update(_code_only(fh.read()).encode())
     text = open(os.path.join(csrc, "rcc_internal.h")).read()
-    for m in re.finditer(r"^typedef [^\n]*;$|^struct AttnArgs \{.*?^\};", text, re.M | re.S):
+    for m in re.finditer(r"^typedef [^\n]*;$|^constexpr int kRawBufferFlags[^\n]*;$|"
+                         r"^struct AttnArgs \{.*?^\};", text, re.M | re.S):
         h.update(_code_only(m.group(0)).encode())
     return h.hexdigest()[:16]
 

@@ -10,7 +10,7 @@
 // What this kernel adds for the bf16 / head_dim-128 shape:
 // * One workgroup of 8 waves (256 query rows, two waves per SIMD) per CU, so
 //   each K/V tile moves from L2 into LDS once per 256 rows.
-// * K and V move global -> LDS with global_load_lds_dwordx4 (no VGPR
+// * K and V move global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //   staging) in 32-key tiles through a ring of four LDS stages: tile t is
 //   computed while tiles t+1 and t+2 are in flight and tile t+3 starts into
 //   the stage tile t-1 used.  One workgroup barrier per tile; the wait before
@@ -68,10 +68,15 @@ __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, uint3
   const int64_t base = (int64_t)jb * row_bytes;
   const int key = min(j0 + 4 * wave + (lane >> 4), kv_end - 1);
   const uint32_t row = (uint32_t)(key - jb) * row_bytes;
-  __builtin_amdgcn_global_load_lds(kg + base + (row + d.k), (lds_void*)(ks + wave * 1024), 16, 0,
-                                   0);
-  __builtin_amdgcn_global_load_lds(vg + base + (row + d.v), (lds_void*)(vs + wave * 1024), 16, 0,
-                                   0);
+  // Raw buffers over the tile's 32 key rows (wave-uniform base): LDS-DMA
+  // through buffer loads, so the LDS fragment reads get exact wait counts.
+  const int32_t span = (int32_t)(kBN * row_bytes);
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kg + base), 0, span, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vg + base), 0, span, kRawBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ks + wave * 1024), 16, row + d.k, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vs + wave * 1024), 16, row + d.v, 0, 0, 0);
 }
 
 template <typename Tout>

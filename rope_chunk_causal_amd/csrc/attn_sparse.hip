@@ -32,12 +32,14 @@
 //   blocks) and only a list's last tile can be partial (its keys past the
 //   stream are masked).  The per-tile MFMA and softmax work is attn_tile.h's,
 //   shared with the dense kernel.
-// * K/V tiles stream global -> LDS with global_load_lds_dwordx4, branch-free
-//   (the tile index is clamped to the last tile, so the wait counts stay
-//   exact), into one __shared__ object per stage.  Row offsets are formed in
-//   64 bits (a wave-uniform base plus 32-bit lane offsets inside a block, or
-//   per lane where a tile spans two blocks), so a batch entry's cache may
-//   exceed 4 GiB.
+// * K/V tiles stream global -> LDS, branch-free (the tile index is clamped
+//   to the last tile, so the wait counts stay exact), into one __shared__
+//   object per stage.  A tile inside one block goes through buffer_load
+//   ... lds from a raw buffer at the tile's wave-uniform 64-bit base with
+//   32-bit lane offsets (exact LDS wait counts, see kRawBufferFlags); a
+//   48-row tile that spans two blocks through global_load_lds_dwordx4 with
+//   each lane's own 64-bit row offset.  So a batch entry's cache may exceed
+//   4 GiB.
 // * Workgroups are numbered XCD-major: the query blocks of one head run on
 //   one XCD and share its L2.
 // * In the grouped kernels only a wave's first key tile takes the checked
@@ -79,15 +81,21 @@ __device__ __forceinline__ void issue_sparse(const char* kg, const char* vg, uin
   t = __builtin_amdgcn_readfirstlane(min(t, n_tiles - 1));
   const int blk = __builtin_amdgcn_readfirstlane(list[t / NW]);
   const int64_t base = (int64_t)(blk * (32 * NW) + (t % NW) * 32) * row_bytes;
+  // Raw buffers over the tile's 32 key rows (see kRawBufferFlags).
+  const int32_t span = (int32_t)(32 * row_bytes);
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kg + base), 0, span, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vg + base), 0, span, kRawBufferFlags);
 #pragma unroll
   for (int j = 0; j < kInstr; ++j) {
     const int i = wave + NW * j;
     const int r = 4 * i + (lane >> 4);
     const uint32_t off = (uint32_t)r * row_bytes;
-    __builtin_amdgcn_global_load_lds(kg + base + (off + k_chunk(r, lane & 15)),
-                                     (lds_void*)(ks + i * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vg + base + (off + v_chunk(r, lane & 15)),
-                                     (lds_void*)(vs + i * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ks + i * 1024), 16,
+                                             off + k_chunk(r, lane & 15), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vs + i * 1024), 16,
+                                             off + v_chunk(r, lane & 15), 0, 0, 0);
   }
 }
 
@@ -271,20 +279,21 @@ __device__ __forceinline__ void issue_list(const char* kg, const char* vg, uint3
     constexpr int kPer = B / 32;
     const int blk = __builtin_amdgcn_readfirstlane(list[t / kPer]);
     const int64_t base = (int64_t)(blk * B + (t % kPer) * 32) * row_bytes;
+    // Raw buffers over the tile's 32 key rows (see kRawBufferFlags).
+    const int32_t span = (int32_t)(32 * row_bytes);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kg + base), 0, span, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vg + base), 0, span, kRawBufferFlags);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int i = i0 + di * j;
       const int r = 4 * i + (lane >> 4);
       const uint32_t off = (uint32_t)r * row_bytes;
-      uint32_t ok = off + k_chunk(r, lane & 15), ov = off + v_chunk(r, lane & 15);
-      // Keeps the compiler from folding the lane offsets into 64-bit lane
-      // pointers outside the tile loop, which turns each load's address into
-      // two 64-bit vector multiply-adds instead of a scalar base plus a
-      // 32-bit offset.  Emits no instruction.
-      asm volatile("" : "+v"(ok), "+v"(ov));
-      __builtin_amdgcn_global_load_lds(kg + base + ok, (lds_void*)(ks + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + base + ov, (lds_void*)(ks + kTileBytes + i * 1024), 16,
-                                       0, 0);
+      const uint32_t ok = off + k_chunk(r, lane & 15), ov = off + v_chunk(r, lane & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ks + i * 1024), 16, ok, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ks + kTileBytes + i * 1024), 16, ov,
+                                               0, 0, 0);
     }
   } else {
     static_assert(B > 32 && B < 64, "a tile spans at most two blocks");

@@ -25,9 +25,10 @@
 //   fewest rounds: a 4680-token chunk is 13 x 18 = 234 workgroups of 384
 //   tokens (one round) against 19 x 18 = 342 of 256 (two rounds).
 // * W and x stream through a ring of LDS stages of 32 K-columns each (W tile
-//   at +0, x tile after it) with global_load_lds_dwordx4: with S stages, tile
-//   t is computed while the next S - 2 are in flight and tile t + S - 1
-//   starts into the stage t - 1 used.  Loads are branch-free (row and k
+//   at +0, x tile after it) with buffer_load_dwordx4 ... lds from raw
+//   buffers over W and x (exact LDS wait counts, see kRawBufferFlags): with
+//   S stages, tile t is computed while the next S - 2 are in flight and tile
+//   t + S - 1 starts into the stage t - 1 used.  Loads are branch-free (row and k
 //   indices clamped), so the compiler tracks which stage each load writes.
 // * Both operands are K-contiguous rows (64 B per row per stage) with the
 //   16-byte chunk swizzle c ^ ((row / 4) % 4), which makes the ds_read_b128
@@ -81,23 +82,30 @@ __device__ __forceinline__ void issue_stage(const __bf16* w, const __bf16* x, in
   k0 = __builtin_amdgcn_readfirstlane(min(k0, K - kBK));
   char* xs = ws + kWTile;
   const uint32_t row_bytes = (uint32_t)(K * 2);
+  // Buffer resources over W and x (each under 4 GiB, checked by the host):
+  // the byte offsets stay 32-bit, and the hardware range check covers the
+  // whole matrix.
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(w), 0, (int)((uint32_t)n_feat * row_bytes), kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(x), 0, (int)((uint32_t)n_tok * row_bytes), kRawBufferFlags);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 32 * wave + 16 * i + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     const uint32_t wrow = (uint32_t)min(f0 + r, n_feat - 1);
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const char*>(w) + (wrow * row_bytes + (uint32_t)(k0 * 2 + c * 16)),
-        (lds_void*)(ws + (2 * wave + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(ws + (2 * wave + i) * 1024), 16,
+                                             wrow * row_bytes + (uint32_t)(k0 * 2 + c * 16), 0,
+                                             0, 0);
   }
 #pragma unroll
   for (int i = 0; i < T::kXInstr; ++i) {
     const int r = 16 * (T::kXInstr * wave + i) + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     const uint32_t xrow = (uint32_t)min(t0 + r, n_tok - 1);
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const char*>(x) + (xrow * row_bytes + (uint32_t)(k0 * 2 + c * 16)),
-        (lds_void*)(xs + (T::kXInstr * wave + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xs + (T::kXInstr * wave + i) * 1024),
+                                             16, xrow * row_bytes + (uint32_t)(k0 * 2 + c * 16),
+                                             0, 0, 0);
   }
 }
 

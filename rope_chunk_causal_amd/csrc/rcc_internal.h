@@ -39,6 +39,14 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Word 3 of the buffer resources the kernels' LDS-DMA loads go through
+// (raw buffers, stride 0): data format 32 bits.  The kernels move K/V and
+// GEMM tiles into LDS with buffer_load ... lds rather than global_load_lds:
+// the compiler's wait-count model then treats LDS reads as completing in
+// order, so a fragment read waits only for itself (lgkmcnt(n)) and not for
+// every LDS read in flight.
+constexpr int kRawBufferFlags = 0x00020000;
+
 // Position of a call's token inside the video ([YL] §3.3.3).  All values
 // fit in 32 bits: the host checks F*H*W < 2^31 and cache rows < 2^31.
 // window == 0: the cache keeps every frame in global order.  window > 0:
