@@ -176,16 +176,9 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
 #pragma unroll
   for (int kk = 1; kk < 8; ++kk) s0 = mfma32(ka[kk], qf[kk], s0);
 
-  if constexpr (kMask) {
-    if (j0 + kBN > lim_lo) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + (r >> 2) * 8 + L.g * 4 + (r & 3);
-        s0[r] = key < L.lim ? s0[r] : -INFINITY;
-      }
-    }
-  }
-
+  // V^T fragments, read before the masking branch so that they share the
+  // S^T MFMAs' basic block and the scheduler can issue them under that chain
+  // (after the branch they waited for the exponentials' block).
   auto vread = [&](int kq, int dt) {
     const int base = kq * 16 * kRowBytes + L.voff[dt];
     // Whole-vector form: building the operand element by element from the
@@ -200,6 +193,16 @@ __device__ __forceinline__ void tile_step(WaveState& w, const Lane& L, const bf1
   for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) vf[kq][dt] = vread(kq, dt);
+
+  if constexpr (kMask) {
+    if (j0 + kBN > lim_lo) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + (r >> 2) * 8 + L.g * 4 + (r & 3);
+        s0[r] = key < L.lim ? s0[r] : -INFINITY;
+      }
+    }
+  }
 
   bf16x8 pf[2];
   if constexpr (kBase2) {
