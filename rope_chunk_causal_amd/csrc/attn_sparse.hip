@@ -36,10 +36,11 @@
 //   to the last tile, so the wait counts stay exact), into one __shared__
 //   object per stage.  A tile inside one block goes through buffer_load
 //   ... lds from a raw buffer at the tile's wave-uniform 64-bit base with
-//   32-bit lane offsets (exact LDS wait counts, see kRawBufferFlags); a
-//   48-row tile that spans two blocks through global_load_lds_dwordx4 with
-//   each lane's own 64-bit row offset.  So a batch entry's cache may exceed
-//   4 GiB.
+//   32-bit lane offsets (exact LDS wait counts, see kRawBufferFlags).  A
+//   48-row tile can span two blocks: while a (batch, head)'s cache rows lie
+//   within 4 GiB of its base, each lane's 32-bit offset goes into one raw
+//   buffer over them; past that, global_load_lds_dwordx4 with each lane's
+//   own 64-bit offset.  So a batch entry's cache may exceed 4 GiB.
 // * Workgroups are numbered XCD-major: the query blocks of one head run on
 //   one XCD and share its L2.
 // * In the grouped kernels only a wave's first key tile takes the checked
@@ -269,10 +270,11 @@ __device__ __forceinline__ int compact_list(const uint32_t* bm, int words, int* 
 // and a wave-uniform 64-bit base plus 32-bit lane offsets address it; for
 // B = 48 a tile spans at most two blocks and each lane forms its row's 64-bit
 // offset itself.
-template <int B, int NI>
+template <int B, int NI, bool kBuf>
 __device__ __forceinline__ void issue_list(const char* kg, const char* vg, uint32_t row_bytes,
                                            const int* list, int n, int t, char* ks, int i0,
-                                           int di, int lane) {
+                                           int di, int lane, __amdgpu_buffer_rsrc_t kall,
+                                           __amdgpu_buffer_rsrc_t vall) {
   const int n_tiles = (n * B + 31) / 32;
   t = __builtin_amdgcn_readfirstlane(min(t, n_tiles - 1));
   if constexpr (B % 32 == 0) {
@@ -310,11 +312,21 @@ __device__ __forceinline__ void issue_list(const char* kg, const char* vg, uint3
       const int gr = min(g0 + r, last);
       const int bi = gr / B;
       const int row = (bi == b_lo ? blk_lo : blk_hi) * B + (gr - bi * B);
-      const int64_t off = (int64_t)row * row_bytes;
-      __builtin_amdgcn_global_load_lds(kg + off + k_chunk(r, lane & 15),
-                                       (lds_void*)(ks + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + off + v_chunk(r, lane & 15),
-                                       (lds_void*)(ks + kTileBytes + i * 1024), 16, 0, 0);
+      if constexpr (kBuf) {
+        // The (batch, head)'s whole cache lies within 4 GiB of its base
+        // (checked by the host): 32-bit offsets into one raw buffer.
+        const uint32_t off = (uint32_t)row * row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kall, (lds_void*)(ks + i * 1024), 16,
+                                                 off + k_chunk(r, lane & 15), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vall, (lds_void*)(ks + kTileBytes + i * 1024),
+                                                 16, off + v_chunk(r, lane & 15), 0, 0, 0);
+      } else {
+        const int64_t off = (int64_t)row * row_bytes;
+        __builtin_amdgcn_global_load_lds(kg + off + k_chunk(r, lane & 15),
+                                         (lds_void*)(ks + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vg + off + v_chunk(r, lane & 15),
+                                         (lds_void*)(ks + kTileBytes + i * 1024), 16, 0, 0);
+      }
     }
   }
 }
@@ -337,9 +349,9 @@ __device__ __forceinline__ void issue_list(const char* kg, const char* vg, uint3
 // three tiles per two blocks, only a list's last tile partial and masked.  A
 // block's second wave holds its rows 32 .. 47; its other 16 rows are
 // computed but not stored.
-template <typename Tout, int NW, int NWB, int B>
+template <typename Tout, int NW, int NWB, int B, bool kBuf>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attn_sparse_grouped_kernel(
-    SparseArgs a, int n_groups) {
+    SparseArgs a, int n_groups, uint32_t span) {
   static_assert(NW == 8 || NW == 4, "4 or 8 waves");
   static_assert(B == 32 * NWB || (B == 48 && NWB == 2), "block of 48, 64, 128 or 256 rows");
   constexpr int kT = 64 * NW;
@@ -390,6 +402,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attn_sparse_grouped_
   const char* vg = reinterpret_cast<const char*>(
       reinterpret_cast<const __bf16*>(a.v) + (int64_t)b * a.cache_tokens * rs + h * kD);
   Tout* og = reinterpret_cast<Tout*>(a.out) + (int64_t)b * a.q_tokens * rs + h * kD;
+  // Raw buffers over the (batch, head)'s whole cache (used by 48-row tiles
+  // when it spans under 4 GiB: span = its byte extent from kg).
+  const __amdgpu_buffer_rsrc_t kall =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kg), 0, (int)span, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t vall =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vg), 0, (int)span, kRawBufferFlags);
 
   const int brow = wq * 32 + l32;       // the lane's row inside its query block
   const int qrow = (qb0 + jw) * B + brow;
@@ -449,7 +467,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attn_sparse_grouped_
   const int np_rows = n_p * B;
   const int n_pt = (np_rows + 31) / 32;
   auto issue_p = [&](int t, char* ks) {
-    issue_list<B, kPI>(kg, vg, row_bytes, s_plist, n_p, t, ks, wave, NW, lane);
+    issue_list<B, kPI, kBuf>(kg, vg, row_bytes, s_plist, n_p, t, ks, wave, NW, lane, kall, vall);
   };
   int n_it = 0;
 #pragma unroll
@@ -495,7 +513,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attn_sparse_grouped_
       const int nl_rows = n_l[J] * B;
       const int my = (nl_rows + 31) / 32;
       auto issue_l = [&](int t, char* ks) {
-        issue_list<B, kLI>(kg, vg, row_bytes, s_llist[J], n_l[J], t, ks, wq, NWB, lane);
+        issue_list<B, kLI, kBuf>(kg, vg, row_bytes, s_llist[J], n_l[J], t, ks, wq, NWB, lane,
+                                  kall, vall);
       };
       // This block's my tiles, then idle barriers up to the group's n_it, so
       // every wave passes the same number of barriers.
@@ -552,8 +571,22 @@ hipError_t launch_grouped(const SparseArgs& a, hipStream_t s) {
   const int n_groups = (a.n_qblocks + G - 1) / G;
   const int64_t total = (int64_t)n_groups * a.n_heads * a.batch;
   if (!grid_fits(total, 64 * NW)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_sparse_grouped_kernel<Tout, NW, NWB, B>), dim3((uint32_t)total),
-                     dim3(64 * NW), 0, s, a, n_groups);
+  // Byte extent of one (batch, head)'s cache rows from its base.  48-row
+  // tiles (which can span two key blocks) load through one raw buffer over
+  // it when it fits 32-bit offsets, else with 64-bit global addresses; the
+  // other block sizes always use per-tile buffers.
+  const int64_t extent = (int64_t)(a.cache_tokens - 1) * a.n_heads * kRowBytes + kRowBytes;
+  const bool narrow = extent <= (int64_t)UINT32_MAX;
+  const uint32_t span = narrow ? (uint32_t)extent : UINT32_MAX;
+  if constexpr (B % 32 != 0) {
+    if (!narrow) {
+      hipLaunchKernelGGL((attn_sparse_grouped_kernel<Tout, NW, NWB, B, false>),
+                         dim3((uint32_t)total), dim3(64 * NW), 0, s, a, n_groups, span);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_sparse_grouped_kernel<Tout, NW, NWB, B, true>),
+                     dim3((uint32_t)total), dim3(64 * NW), 0, s, a, n_groups, span);
   return hipGetLastError();
 }
 
